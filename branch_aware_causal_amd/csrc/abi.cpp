@@ -1,0 +1,242 @@
+// C ABI of libbac: argument validation, error state and kernel dispatch.
+// Every entry point validates host-visible arguments before enqueuing any
+// device work and reports problems through a status code plus a thread-local
+// message; nothing here throws or aborts.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/bac.h"
+#include "abi_internal.hpp"
+#include "launch.hpp"
+
+namespace bac {
+
+static thread_local std::string g_error;
+
+void clear_error() { g_error.clear(); }
+
+bac_status fail(bac_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+static bac_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return BAC_OK;
+  return fail(BAC_EHIP, "%s: HIP error %d (%s)", where, static_cast<int>(e), hipGetErrorString(e));
+}
+
+// Optional override of the bf16 main-attention implementation: the
+// BAC_MAIN_IMPL environment variable set to "valu" selects the vector-ALU
+// kernels (a slow second GPU implementation used for cross-checks).
+static bool main_uses_valu(int dt) {
+  if (dt == kF32) return true;
+  const char* e = std::getenv("BAC_MAIN_IMPL");
+  return e && std::strcmp(e, "valu") == 0;
+}
+
+static bac_status check_heads(const char* fn, int32_t hq, int32_t hkv, int32_t d, int32_t dt) {
+  if (hq < 1 || hkv < 1) return fail(BAC_EINVAL, "%s: hq=%d hkv=%d must be >= 1", fn, hq, hkv);
+  if (hq % hkv != 0) return fail(BAC_EINVAL, "%s: hq=%d is not a multiple of hkv=%d", fn, hq, hkv);
+  if (32 % (hq / hkv) != 0)
+    return fail(BAC_EUNSUPPORTED, "%s: GQA ratio hq/hkv=%d must divide 32", fn, hq / hkv);
+  if (d != 64 && d != 128) return fail(BAC_EUNSUPPORTED, "%s: head dim %d not in {64, 128}", fn, d);
+  if (dt != BAC_F32 && dt != BAC_BF16) return fail(BAC_EINVAL, "%s: unknown dtype %d", fn, dt);
+  return BAC_OK;
+}
+
+static bac_status check_count(const char* fn, const char* what, int32_t n, int32_t heads) {
+  if (n < 0) return fail(BAC_EINVAL, "%s: %s=%d is negative", fn, what, n);
+  if (static_cast<int64_t>(n) * heads > INT32_MAX)
+    return fail(BAC_ESIZE, "%s: %s*heads exceeds 2^31", fn, what);
+  return BAC_OK;
+}
+
+#define BAC_TRY(expr)              \
+  do {                             \
+    bac_status _st = (expr);       \
+    if (_st != BAC_OK) return _st; \
+  } while (0)
+
+static bac_status check_main(const char* fn, const void* q, const int32_t* q_seq,
+                             const int32_t* q_pos, int32_t nq, const void* k, const void* v,
+                             const int32_t* k_seq, const int32_t* k_pos, int32_t nk, int32_t hq,
+                             int32_t hkv, int32_t d, int32_t dt, float scale) {
+  BAC_TRY(check_heads(fn, hq, hkv, d, dt));
+  BAC_TRY(check_count(fn, "nq", nq, hq));
+  BAC_TRY(check_count(fn, "nk", nk, hq));
+  if (nq > 0 && (!q || !q_seq || !q_pos)) return fail(BAC_EINVAL, "%s: null query array", fn);
+  if (nk > 0 && (!k || !v || !k_seq || !k_pos)) return fail(BAC_EINVAL, "%s: null key array", fn);
+  if (!std::isfinite(scale)) return fail(BAC_EINVAL, "%s: scale is not finite", fn);
+  return BAC_OK;
+}
+
+static bac_status check_branch(const char* fn, const void* qb, const void* kb, const void* vb,
+                               int32_t nb, const int32_t* branch_cu, int32_t num_branches,
+                               int32_t max_len, int32_t kind, int32_t hq, int32_t hkv, int32_t d,
+                               int32_t dt, float scale) {
+  BAC_TRY(check_heads(fn, hq, hkv, d, dt));
+  BAC_TRY(check_count(fn, "nb", nb, hq));
+  if (num_branches < 0) return fail(BAC_EINVAL, "%s: num_branches=%d is negative", fn, num_branches);
+  if (num_branches > 0 && !branch_cu) return fail(BAC_EINVAL, "%s: null branch_cu", fn);
+  if (nb > 0 && (!qb || !kb || !vb)) return fail(BAC_EINVAL, "%s: null branch tensor", fn);
+  if (kind != BAC_BRANCH_CAUSAL && kind != BAC_BRANCH_BIDIR)
+    return fail(BAC_EINVAL, "%s: unknown branch kind %d", fn, kind);
+  if (max_len < 1 || max_len > 32)
+    return fail(BAC_EUNSUPPORTED, "%s: max_branch_len=%d outside [1, 32]", fn, max_len);
+  if (!std::isfinite(scale)) return fail(BAC_EINVAL, "%s: scale is not finite", fn);
+  return BAC_OK;
+}
+
+}  // namespace bac
+
+using namespace bac;
+
+extern "C" {
+
+const char* bac_last_error(void) { return g_error.c_str(); }
+
+int32_t bac_version(void) { return 100; }
+
+bac_status attn_main_fwd(const void* q, const int32_t* q_seq, const int32_t* q_pos, int32_t nq,
+                         const void* k, const void* v, const int32_t* k_seq, const int32_t* k_pos,
+                         int32_t nk, int32_t hq, int32_t hkv, int32_t d, bac_dtype dt, float scale,
+                         float* o_acc, float* lse, bac_acc_mode mode, void* o_out, void* stream) {
+  clear_error();
+  const char* fn = "attn_main_fwd";
+  BAC_TRY(check_main(fn, q, q_seq, q_pos, nq, k, v, k_seq, k_pos, nk, hq, hkv, d, dt, scale));
+  if (mode != BAC_WRITE && mode != BAC_MERGE) return fail(BAC_EINVAL, "%s: unknown mode %d", fn, mode);
+  if (nq > 0 && (!o_acc || !lse)) return fail(BAC_EINVAL, "%s: null o_acc or lse", fn);
+  if (nq == 0) return BAC_OK;
+  MainArgs a{};
+  a.q = q; a.q_seq = q_seq; a.q_pos = q_pos; a.nq = nq;
+  a.k = k; a.v = v; a.k_seq = k_seq; a.k_pos = k_pos; a.nk = nk;
+  a.hq = hq; a.hkv = hkv; a.d = d; a.dt = dt; a.scale = scale;
+  a.o_acc = o_acc; a.lse_acc = lse; a.mode = mode; a.o_out = o_out;
+  a.stream = static_cast<hipStream_t>(stream);
+  hipError_t e = main_uses_valu(dt) ? launch_main_fwd_valu(a) : launch_main_fwd_mfma(a);
+  return hip_status(e, fn);
+}
+
+bac_status attn_branch_fwd(const void* qb, const void* kb, const void* vb, int32_t nb,
+                           const int32_t* branch_cu, int32_t num_branches, int32_t max_branch_len,
+                           bac_branch_kind kind, int32_t hq, int32_t hkv, int32_t d, bac_dtype dt,
+                           float scale, float* o_acc, float* lse, bac_acc_mode mode, void* o_out,
+                           void* stream) {
+  clear_error();
+  const char* fn = "attn_branch_fwd";
+  BAC_TRY(check_branch(fn, qb, kb, vb, nb, branch_cu, num_branches, max_branch_len, kind, hq, hkv,
+                       d, dt, scale));
+  if (mode != BAC_WRITE && mode != BAC_MERGE) return fail(BAC_EINVAL, "%s: unknown mode %d", fn, mode);
+  if (nb > 0 && (!o_acc || !lse)) return fail(BAC_EINVAL, "%s: null o_acc or lse", fn);
+  if (nb == 0 || num_branches == 0) return BAC_OK;
+  BranchArgs a{};
+  a.qb = qb; a.kb = kb; a.vb = vb; a.nb = nb;
+  a.branch_cu = branch_cu; a.num_branches = num_branches; a.max_len = max_branch_len;
+  a.bidir = kind == BAC_BRANCH_BIDIR;
+  a.hq = hq; a.hkv = hkv; a.d = d; a.dt = dt; a.scale = scale;
+  a.o_acc = o_acc; a.lse_acc = lse; a.mode = mode; a.o_out = o_out;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(launch_branch_fwd(a), fn);
+}
+
+bac_status lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
+                     int32_t n, int32_t hq, int32_t d, bac_dtype out_dt, void* o_out,
+                     void* stream) {
+  clear_error();
+  const char* fn = "lse_merge";
+  if (hq < 1) return fail(BAC_EINVAL, "%s: hq=%d must be >= 1", fn, hq);
+  if (d != 64 && d != 128) return fail(BAC_EUNSUPPORTED, "%s: head dim %d not in {64, 128}", fn, d);
+  BAC_TRY(check_count(fn, "n", n, hq));
+  if (out_dt != BAC_F32 && out_dt != BAC_BF16) return fail(BAC_EINVAL, "%s: unknown dtype", fn);
+  if (n > 0 && (!o_acc || !lse_acc || !o_part || !lse_part))
+    return fail(BAC_EINVAL, "%s: null accumulator or part", fn);
+  if (n > 0 && o_acc == o_part) return fail(BAC_EINVAL, "%s: o_part aliases o_acc", fn);
+  if (n == 0) return BAC_OK;
+  return hip_status(launch_lse_merge(o_acc, lse_acc, o_part, lse_part, n, hq, d, out_dt, o_out,
+                                     static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+bac_status attn_bwd_delta(const void* o, bac_dtype o_dt, const void* dout, bac_dtype dt, int32_t n,
+                          int32_t hq, int32_t d, float* delta, void* stream) {
+  clear_error();
+  const char* fn = "attn_bwd_delta";
+  if (hq < 1) return fail(BAC_EINVAL, "%s: hq=%d must be >= 1", fn, hq);
+  if (d != 64 && d != 128) return fail(BAC_EUNSUPPORTED, "%s: head dim %d not in {64, 128}", fn, d);
+  BAC_TRY(check_count(fn, "n", n, hq));
+  if ((o_dt != BAC_F32 && o_dt != BAC_BF16) || (dt != BAC_F32 && dt != BAC_BF16))
+    return fail(BAC_EINVAL, "%s: unknown dtype", fn);
+  if (n > 0 && (!o || !dout || !delta)) return fail(BAC_EINVAL, "%s: null pointer", fn);
+  if (n == 0) return BAC_OK;
+  return hip_status(launch_delta(o, o_dt, dout, dt, n, hq, d, delta, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+bac_status attn_main_bwd(const void* q, const int32_t* q_seq, const int32_t* q_pos, int32_t nq,
+                         const void* k, const void* v, const int32_t* k_seq, const int32_t* k_pos,
+                         int32_t nk, int32_t hq, int32_t hkv, int32_t d, bac_dtype dt, float scale,
+                         const void* dout, const float* lse, const float* delta, float* dq_acc,
+                         float* dk_acc, float* dv_acc, void* stream) {
+  clear_error();
+  const char* fn = "attn_main_bwd";
+  BAC_TRY(check_main(fn, q, q_seq, q_pos, nq, k, v, k_seq, k_pos, nk, hq, hkv, d, dt, scale));
+  if (nq > 0 && (!dout || !lse || !delta || !dq_acc))
+    return fail(BAC_EINVAL, "%s: null dout, lse, delta or dq_acc", fn);
+  if (nk > 0 && (!dk_acc || !dv_acc)) return fail(BAC_EINVAL, "%s: null dk_acc or dv_acc", fn);
+  if (nq == 0 || nk == 0) return BAC_OK;
+  MainArgs a{};
+  a.q = q; a.q_seq = q_seq; a.q_pos = q_pos; a.nq = nq;
+  a.k = k; a.v = v; a.k_seq = k_seq; a.k_pos = k_pos; a.nk = nk;
+  a.hq = hq; a.hkv = hkv; a.d = d; a.dt = dt; a.scale = scale;
+  a.dout = dout; a.lse = lse; a.delta = delta; a.dq = dq_acc; a.dk = dk_acc; a.dv = dv_acc;
+  a.stream = static_cast<hipStream_t>(stream);
+  hipError_t e = main_uses_valu(dt) ? launch_main_bwd_valu(a) : launch_main_bwd_mfma(a);
+  return hip_status(e, fn);
+}
+
+bac_status attn_branch_bwd(const void* qb, const void* kb, const void* vb, int32_t nb,
+                           const int32_t* branch_cu, int32_t num_branches, int32_t max_branch_len,
+                           bac_branch_kind kind, int32_t hq, int32_t hkv, int32_t d, bac_dtype dt,
+                           float scale, const void* doutb, const float* lseb, const float* deltab,
+                           float* dqb_acc, float* dkb_acc, float* dvb_acc, void* stream) {
+  clear_error();
+  const char* fn = "attn_branch_bwd";
+  BAC_TRY(check_branch(fn, qb, kb, vb, nb, branch_cu, num_branches, max_branch_len, kind, hq, hkv,
+                       d, dt, scale));
+  if (nb > 0 && (!doutb || !lseb || !deltab || !dqb_acc || !dkb_acc || !dvb_acc))
+    return fail(BAC_EINVAL, "%s: null gradient argument", fn);
+  if (nb == 0 || num_branches == 0) return BAC_OK;
+  BranchArgs a{};
+  a.qb = qb; a.kb = kb; a.vb = vb; a.nb = nb;
+  a.branch_cu = branch_cu; a.num_branches = num_branches; a.max_len = max_branch_len;
+  a.bidir = kind == BAC_BRANCH_BIDIR;
+  a.hq = hq; a.hkv = hkv; a.d = d; a.dt = dt; a.scale = scale;
+  a.dout = doutb; a.lse = lseb; a.delta = deltab; a.dq = dqb_acc; a.dk = dkb_acc; a.dv = dvb_acc;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(launch_branch_bwd(a), fn);
+}
+
+bac_status attn_check_index(const int32_t* seq, const int32_t* pos, int32_t n, int32_t strict,
+                            int32_t* bad_count, void* stream) {
+  clear_error();
+  const char* fn = "attn_check_index";
+  if (n < 0) return fail(BAC_EINVAL, "%s: n=%d is negative", fn, n);
+  if (!bad_count || (n > 0 && (!seq || !pos))) return fail(BAC_EINVAL, "%s: null pointer", fn);
+  return hip_status(launch_check_index(seq, pos, n, strict ? 1 : 0, bad_count,
+                                       static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+}  // extern "C"

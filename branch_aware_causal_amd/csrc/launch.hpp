@@ -1,0 +1,84 @@
+// Internal launcher interface between the C ABI (abi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bac {
+
+enum DType : int { kF32 = 0, kBF16 = 1 };
+
+// One main-attention call: query rows against one K/V shard.
+struct MainArgs {
+  const void* q;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  int nq;
+  const void* k;
+  const void* v;
+  const int32_t* k_seq;
+  const int32_t* k_pos;
+  int nk;
+  int hq, hkv, d;
+  int dt;
+  float scale;
+  // forward
+  float* o_acc;
+  float* lse_acc;
+  int mode;            // 0 write, 1 merge
+  void* o_out;
+  // backward
+  const void* dout;
+  const float* lse;
+  const float* delta;
+  float* dq;
+  float* dk;
+  float* dv;
+  hipStream_t stream;
+};
+
+// One branch-attention call over rank-local branches.
+struct BranchArgs {
+  const void* qb;
+  const void* kb;
+  const void* vb;
+  int nb;
+  const int32_t* branch_cu;
+  int num_branches;
+  int max_len;
+  int bidir;
+  int hq, hkv, d;
+  int dt;
+  float scale;
+  float* o_acc;
+  float* lse_acc;
+  int mode;
+  void* o_out;
+  const void* dout;
+  const float* lse;
+  const float* delta;
+  float* dq;
+  float* dk;
+  float* dv;
+  hipStream_t stream;
+};
+
+hipError_t launch_main_fwd_valu(const MainArgs& a);
+hipError_t launch_main_bwd_valu(const MainArgs& a);
+hipError_t launch_main_fwd_mfma(const MainArgs& a);
+hipError_t launch_main_bwd_mfma(const MainArgs& a);
+hipError_t launch_branch_fwd(const BranchArgs& a);
+hipError_t launch_branch_bwd(const BranchArgs& a);
+hipError_t launch_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
+                            int n, int hq, int d, int out_dt, void* o_out, hipStream_t s);
+hipError_t launch_delta(const void* o, int o_dt, const void* dout, int dt, int n, int hq, int d,
+                        float* delta, hipStream_t s);
+hipError_t launch_check_index(const int32_t* seq, const int32_t* pos, int n, int strict,
+                              int32_t* bad, hipStream_t s);
+
+// Bytes of dynamic LDS the branch backward needs per workgroup.
+inline size_t branch_bwd_lds_bytes(int max_len, int d) {
+  return static_cast<size_t>(max_len) * d * 2 * sizeof(float);
+}
+
+}  // namespace bac

@@ -1,0 +1,516 @@
+// attn_main_bwd, bf16 on MFMA (gfx950).
+//
+// Gradients of one ring step's main part, recomputed from the merged lse of
+// each row (P = exp2(s*c - lse2)); the pages leave the backward open, so this
+// is the vector-Jacobian product of the forward for upstream dO:
+//   dS = P (dP - Delta),  dP = dO V^T,
+//   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO  (dK/dV summed over the
+//   q-heads of a GQA group).
+//
+// Two kernels, no atomics (deterministic):
+//   * dq kernel, query-outer like the forward: 8 waves x 32 (token, head)
+//     rows stream the visible K/V tiles; S^T = K Q^T and dP^T = V dO^T keep one
+//     query row per lane, dQ^T += K^T dS^T reads a transposed K tile.
+//   * dkdv kernel, key-outer: 4 waves x 32 keys hold K and V as MFMA operands
+//     in registers and stream the query rows that can see them in tiles of 32
+//     rows; S = Q K^T and dP = dO V^T keep one key per lane, dV^T += dO^T P and
+//     dK^T += Q^T dS read transposed Q / dO tiles.
+// Every workgroup owns its output rows, so the += into the fp32 accumulators
+// is race-free within a launch and ordered across launches on one stream.
+
+#include <climits>
+
+#include "launch.hpp"
+#include "mfma_common.hpp"
+
+namespace bac {
+
+namespace bwdq {
+constexpr int BN = 64;
+constexpr int NW = 8;
+constexpr int PAD = 8;
+}  // namespace bwdq
+
+template <int D, int G>
+__global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_pos, int nq, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ k_seq,
+    const int32_t* __restrict__ k_pos, int nk, int hq, int hkv, float scale,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ delta, float* __restrict__ dq) {
+  using namespace bwdq;
+  constexpr int TPW = 32 / G;
+  constexpr int TPB = NW * TPW;
+  constexpr int KS = D / 16;
+  constexpr int MB = D / 32;
+  constexpr int KROW = D + PAD;
+  constexpr int TROW = BN + PAD;
+  constexpr int CPR = D / 8;
+  constexpr int LOADS = BN * CPR / 512;
+
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KROW];   // keys (perm rows) x d
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * KROW];   // keys (perm rows) x d
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][D * TROW];    // d x keys
+  __shared__ __attribute__((aligned(16))) int kseq_s[2][BN];
+  __shared__ __attribute__((aligned(16))) int kpos_s[2][BN];
+
+  const float scale_log2 = scale * kLog2e;
+  const int nblk_tok = (nq + TPB - 1) / TPB;
+  const int L = xcd_remap(blockIdx.x, nblk_tok * hkv);
+  const int g = L / nblk_tok;
+  const int tb = nblk_tok - 1 - (L % nblk_tok);
+  const int tok0 = tb * TPB;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, hi = lane >> 5;
+
+  const int wtok0 = tok0 + wave * TPW;
+  const int my_tok = wtok0 + n / G;
+  const int my_head = g * G + n % G;
+  const bool row_valid = my_tok < nq;
+  const int my_seq = row_valid ? q_seq[my_tok] : 0;
+  const int my_pos = row_valid ? q_pos[my_tok] : 0;
+  const size_t li = static_cast<size_t>(my_head) * nq + my_tok;
+  const float my_lse2 = row_valid ? lse[li] * kLog2e : kNegInf;
+  const float my_delta = row_valid ? delta[li] : 0.f;
+  const bool row_live = row_valid && my_lse2 != kNegInf;
+
+  const int wlast = min(nq, wtok0 + TPW) - 1;
+  const bool wave_valid = wtok0 < nq;
+  const bool wave_complete = wtok0 + TPW <= nq;
+  const int wf_seq = wave_valid ? q_seq[wtok0] : 0, wf_pos = wave_valid ? q_pos[wtok0] : 0;
+  const int wl_seq = wave_valid ? q_seq[wlast] : 0, wl_pos = wave_valid ? q_pos[wlast] : 0;
+
+  const int blast = min(nq, tok0 + TPB) - 1;
+  const int lo = lower_bound_sp(k_seq, k_pos, nk, q_seq[tok0], INT_MIN);
+  const int hi_k = upper_bound_sp(k_seq, k_pos, nk, q_seq[blast], q_pos[blast]);
+  const int ntiles = hi_k > lo ? (hi_k - lo + BN - 1) / BN : 0;
+
+  bf16x8 qreg[KS], doreg[KS];
+  {
+    const size_t off = (static_cast<size_t>(my_tok) * hq + my_head) * D + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qreg[ks] = row_valid ? *reinterpret_cast<const bf16x8*>(q + off + 16 * ks) : zero8();
+      doreg[ks] = row_valid ? *reinterpret_cast<const bf16x8*>(dout + off + 16 * ks) : zero8();
+    }
+  }
+  f32x16 dqacc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) dqacc[mb] = zero16();
+
+  uint4 kreg[LOADS], vreg[LOADS];
+  int sreg = 0, preg = 0;
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
+      const int c = tid + 512 * it;
+      const int key = c / CPR, col = (c % CPR) * 8;
+      const int j = j0 + key;
+      if (j < nk) {
+        const size_t off = (static_cast<size_t>(j) * hkv + g) * D + col;
+        kreg[it] = *reinterpret_cast<const uint4*>(k + off);
+        vreg[it] = *reinterpret_cast<const uint4*>(v + off);
+      } else {
+        kreg[it] = make_uint4(0, 0, 0, 0);
+        vreg[it] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    if (tid < BN) {
+      const int j = j0 + tid;
+      const bool ok = j < hi_k;
+      sreg = ok ? k_seq[j] : INT_MIN;
+      preg = ok ? k_pos[j] : INT_MAX;
+    }
+  };
+  auto store_tile = [&](int b) {
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
+      const int c = tid + 512 * it;
+      const int key = c / CPR, col = (c % CPR) * 8;
+      *reinterpret_cast<uint4*>(&Ks[b][perm_row(key) * KROW + col]) = kreg[it];
+      *reinterpret_cast<uint4*>(&Vs[b][perm_row(key) * KROW + col]) = vreg[it];
+      const uint32_t w[4] = {kreg[it].x, kreg[it].y, kreg[it].z, kreg[it].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        Kt[b][(col + e) * TROW + key] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+    }
+    if (tid < BN) {
+      kseq_s[b][tid] = sreg;
+      kpos_s[b][tid] = preg;
+    }
+  };
+
+  if (ntiles > 0) {
+    load_tile(lo);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int b = t & 1;
+    const int j0 = lo + t * BN;
+    if (t + 1 < ntiles) load_tile(j0 + BN);
+
+    const int jl = min(hi_k, j0 + BN) - 1 - j0;
+    const int kf_seq = kseq_s[b][0], kf_pos = kpos_s[b][0];
+    const int kl_seq = kseq_s[b][jl], kl_pos = kpos_s[b][jl];
+    const bool wave_any = wave_valid && !lex_less(wl_seq, wl_pos, kf_seq, kf_pos) &&
+                          !lex_less(kl_seq, kl_pos, wf_seq, INT_MIN);
+    const bool wave_full = wave_complete && jl == BN - 1 && kf_seq == kl_seq &&
+                           kf_seq == wf_seq && wf_seq == wl_seq && kl_pos <= wf_pos;
+
+    if (wave_any) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 sacc = zero16(), dpacc = zero16();
+        const uint16_t* kp = &Ks[b][(kb * 32 + n) * KROW + 8 * hi];
+        const uint16_t* vp = &Vs[b][(kb * 32 + n) * KROW + 8 * hi];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          sacc = mfma32(lds_read8(kp + 16 * ks), qreg[ks], sacc);
+          dpacc = mfma32(lds_read8(vp + 16 * ks), doreg[ks], dpacc);
+        }
+        // lane (n, hi) holds keys kb*32 + 16*hi + r of row n
+        float ds[16];
+        const int tb0 = kb * 32 + 16 * hi;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          int sv[4] = {0, 0, 0, 0}, pv[4] = {0, 0, 0, 0};
+          if (!wave_full) {
+            const int4 ss = *reinterpret_cast<const int4*>(&kseq_s[b][tb0 + 4 * r4]);
+            const int4 pp = *reinterpret_cast<const int4*>(&kpos_s[b][tb0 + 4 * r4]);
+            sv[0] = ss.x; sv[1] = ss.y; sv[2] = ss.z; sv[3] = ss.w;
+            pv[0] = pp.x; pv[1] = pp.y; pv[2] = pp.z; pv[3] = pp.w;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e;
+            const bool vis = row_live && (wave_full || (sv[e] == my_seq && pv[e] <= my_pos));
+            const float p = vis ? exp2_fast(sacc[r] * scale_log2 - my_lse2) : 0.f;
+            ds[r] = p * (dpacc[r] - my_delta);
+          }
+        }
+        // dQ^T += K^T dS^T over the 32 keys of this block (2 k-steps)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const bf16x8 db = pack8(&ds[8 * s2]);
+          const uint16_t* tp = &Kt[b][n * TROW + kb * 32 + 16 * hi + 8 * s2];
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) dqacc[mb] = mfma32(lds_read8(tp + mb * 32 * TROW), db, dqacc[mb]);
+        }
+      }
+    }
+
+    if (t + 1 < ntiles) store_tile(b ^ 1);
+    __syncthreads();
+  }
+
+  if (!row_valid) return;
+  const size_t obase = (static_cast<size_t>(my_tok) * hq + my_head) * D;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      float4* p = reinterpret_cast<float4*>(dq + obase + mb * 32 + 8 * gq + 4 * hi);
+      float4 a = *p;
+      a.x += scale * dqacc[mb][4 * gq + 0];
+      a.y += scale * dqacc[mb][4 * gq + 1];
+      a.z += scale * dqacc[mb][4 * gq + 2];
+      a.w += scale * dqacc[mb][4 * gq + 3];
+      *p = a;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV: key-outer.
+// ---------------------------------------------------------------------------
+namespace bwdkv {
+constexpr int NW = 4;          // waves per workgroup, 32 keys each
+constexpr float kSplitP = 1.f / 256.f;
+constexpr int KB = NW * 32;    // keys per workgroup
+constexpr int PAD = 8;
+}  // namespace bwdkv
+
+template <int D, int G>
+__global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_pos, int nq, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ k_seq,
+    const int32_t* __restrict__ k_pos, int nk, int hq, int hkv, float scale,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv) {
+  using namespace bwdkv;
+  constexpr int TPT = 32 / G;          // tokens per 32-row query tile
+  constexpr int KS = D / 16;
+  constexpr int MB = D / 32;
+  constexpr int RROW = D + PAD;        // row-major tile stride
+  constexpr int TROW = 32 + PAD;       // transposed tile stride
+  constexpr int CPR = D / 8;
+  constexpr int LOADS = 32 * CPR / 256;   // 16-byte chunks per thread per tile (per tensor)
+
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][32 * RROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Ds[2][32 * RROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][D * TROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Dt[2][D * TROW];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][32];
+  __shared__ __attribute__((aligned(16))) float dl_s[2][32];
+  __shared__ __attribute__((aligned(16))) int rseq_s[2][32];
+  __shared__ __attribute__((aligned(16))) int rpos_s[2][32];
+
+  const float scale_log2 = scale * kLog2e;
+  const int nblk = (nk + KB - 1) / KB;
+  const int L = xcd_remap(blockIdx.x, nblk * hkv);
+  const int g = L / nblk;
+  const int kblk = L % nblk;             // early keys are seen by the most rows: heavy first
+  const int key0 = kblk * KB;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, hi = lane >> 5;
+
+  // this lane's key
+  const int my_key = key0 + wave * 32 + n;
+  const bool key_valid = my_key < nk;
+  const int kseq = key_valid ? k_seq[my_key] : INT_MIN;
+  const int kpos = key_valid ? k_pos[my_key] : INT_MAX;
+  // wave-level key summary (keys sorted)
+  const int wk0 = key0 + wave * 32;
+  const bool wave_valid = wk0 < nk;
+  const int wkl = min(nk, wk0 + 32) - 1;
+  const bool wave_complete = wk0 + 32 <= nk;
+  const int wf_seq = wave_valid ? k_seq[wk0] : 0, wf_pos = wave_valid ? k_pos[wk0] : 0;
+  const int wl_seq = wave_valid ? k_seq[wkl] : 0, wl_pos = wave_valid ? k_pos[wkl] : 0;
+
+  // K and V of this lane's key as B operands: key n, d = 16*ks + 8*hi + 0..7
+  bf16x8 kreg[KS], vreg[KS];
+  {
+    const size_t off = (static_cast<size_t>(my_key) * hkv + g) * D + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kreg[ks] = key_valid ? *reinterpret_cast<const bf16x8*>(k + off + 16 * ks) : zero8();
+      vreg[ks] = key_valid ? *reinterpret_cast<const bf16x8*>(v + off + 16 * ks) : zero8();
+    }
+  }
+
+  // query tokens that can see any key of the block
+  const int klast = min(nk, key0 + KB) - 1;
+  const int qlo = lower_bound_sp(q_seq, q_pos, nq, k_seq[key0], k_pos[key0]);
+  const int qhi = upper_bound_sp(q_seq, q_pos, nq, k_seq[klast], INT_MAX);
+  const int ntiles = qhi > qlo ? (qhi - qlo + TPT - 1) / TPT : 0;
+
+  f32x16 dkacc[MB], dvacc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    dkacc[mb] = zero16();
+    dvacc[mb] = zero16();
+  }
+
+  // staging: thread -> (row = tid % 32, chunk = tid / 32 + 8 * it); a row is
+  // (token t0 + row / G, head g*G + row % G)
+  uint4 qr[LOADS], dr[LOADS];
+  float lreg = 0.f, dlreg = 0.f;
+  int sreg = 0, preg = 0;
+  auto load_tile = [&](int t0) {
+    const int row = tid & 31;
+    const int tok = t0 + row / G;
+    const int head = g * G + row % G;
+    const bool ok = tok < qhi;
+    const size_t base = (static_cast<size_t>(tok) * hq + head) * D;
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
+      const int col = ((tid >> 5) + 8 * it) * 8;
+      qr[it] = ok ? *reinterpret_cast<const uint4*>(q + base + col) : make_uint4(0, 0, 0, 0);
+      dr[it] = ok ? *reinterpret_cast<const uint4*>(dout + base + col) : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < 32) {
+      const size_t li = static_cast<size_t>(head) * nq + tok;
+      lreg = ok ? lse[li] * kLog2e : kNegInf;
+      dlreg = ok ? delta[li] : 0.f;
+      sreg = ok ? q_seq[tok] : INT_MAX;
+      preg = ok ? q_pos[tok] : INT_MIN;
+    }
+  };
+  auto store_tile = [&](int b) {
+    const int row = tid & 31;
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
+      const int col = ((tid >> 5) + 8 * it) * 8;
+      *reinterpret_cast<uint4*>(&Qs[b][perm_row(row) * RROW + col]) = qr[it];
+      *reinterpret_cast<uint4*>(&Ds[b][perm_row(row) * RROW + col]) = dr[it];
+      const uint32_t wq[4] = {qr[it].x, qr[it].y, qr[it].z, qr[it].w};
+      const uint32_t wd[4] = {dr[it].x, dr[it].y, dr[it].z, dr[it].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        Qt[b][(col + e) * TROW + row] = static_cast<uint16_t>(wq[e >> 1] >> (16 * (e & 1)));
+        Dt[b][(col + e) * TROW + row] = static_cast<uint16_t>(wd[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+    if (tid < 32) {
+      lse_s[b][tid] = lreg;
+      dl_s[b][tid] = dlreg;
+      rseq_s[b][tid] = sreg;
+      rpos_s[b][tid] = preg;
+    }
+  };
+
+  if (ntiles > 0) {
+    load_tile(qlo);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int b = t & 1;
+    const int t0 = qlo + t * TPT;
+    if (t + 1 < ntiles) load_tile(t0 + TPT);
+
+    // tile rows 0..31 are sorted by (seq, pos); row 31 may be padding
+    const int rl = min(qhi - t0, TPT) * G - 1;     // last valid row
+    const int rf_seq = rseq_s[b][0], rf_pos = rpos_s[b][0];
+    const int rl_seq = rseq_s[b][rl], rl_pos = rpos_s[b][rl];
+    const bool wave_any = wave_valid && !lex_less(rl_seq, rl_pos, wf_seq, wf_pos) &&
+                          !lex_less(wl_seq, INT_MAX, rf_seq, rf_pos);
+    const bool wave_full = wave_complete && rl == 31 && rf_seq == rl_seq && rf_seq == wf_seq &&
+                           wf_seq == wl_seq && rf_pos >= wl_pos;
+
+    if (wave_any) {
+      f32x16 sacc = zero16(), dpacc = zero16();
+      const uint16_t* qp = &Qs[b][n * RROW + 8 * hi];
+      const uint16_t* dp = &Ds[b][n * RROW + 8 * hi];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sacc = mfma32(lds_read8(qp + 16 * ks), kreg[ks], sacc);
+        dpacc = mfma32(lds_read8(dp + 16 * ks), vreg[ks], dpacc);
+      }
+      // lane (n = key, hi) holds rows 16*hi + r
+      float p[16], ds[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int rb = 16 * hi + 4 * r4;
+        const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[b][rb]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&dl_s[b][rb]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        int sv[4] = {0, 0, 0, 0}, pv[4] = {0, 0, 0, 0};
+        if (!wave_full) {
+          const int4 ss = *reinterpret_cast<const int4*>(&rseq_s[b][rb]);
+          const int4 pp = *reinterpret_cast<const int4*>(&rpos_s[b][rb]);
+          sv[0] = ss.x; sv[1] = ss.y; sv[2] = ss.z; sv[3] = ss.w;
+          pv[0] = pp.x; pv[1] = pp.y; pv[2] = pp.z; pv[3] = pp.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          const bool vis = key_valid && lv[e] != kNegInf &&
+                           (wave_full || (sv[e] == kseq && pv[e] >= kpos));
+          const float pr = vis ? exp2_fast(sacc[r] * scale_log2 - lv[e]) : 0.f;
+          p[r] = pr;
+          ds[r] = pr * (dpacc[r] - dv4[e]);
+        }
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS  (k = 32 rows, 2 steps of 16).
+      // P and dS enter the MFMA as bf16.  Where some P of the block reaches
+      // kSplitP, they enter as hi + lo bf16 pairs (lo = x - hi, a second MFMA
+      // on the same A operand): rows that give a key a large weight would
+      // otherwise carry bf16's 2^-9 relative rounding into the key's gradient
+      // with a large coefficient.  Below the threshold the dropped lo terms
+      // are at most kSplitP * 2^-9 each.
+      bool big = false;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) big |= p[r] >= kSplitP;
+      const bool split = __any(big);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        float ph[8], dh[8];
+        bf16x8 pb, db;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pb[j] = static_cast<__bf16>(p[8 * s2 + j]);
+          db[j] = static_cast<__bf16>(ds[8 * s2 + j]);
+          ph[j] = p[8 * s2 + j] - static_cast<float>(pb[j]);
+          dh[j] = ds[8 * s2 + j] - static_cast<float>(db[j]);
+        }
+        const uint16_t* dtp = &Dt[b][n * TROW + 16 * hi + 8 * s2];
+        const uint16_t* qtp = &Qt[b][n * TROW + 16 * hi + 8 * s2];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const bf16x8 at = lds_read8(dtp + mb * 32 * TROW);
+          const bf16x8 aq = lds_read8(qtp + mb * 32 * TROW);
+          dvacc[mb] = mfma32(at, pb, dvacc[mb]);
+          dkacc[mb] = mfma32(aq, db, dkacc[mb]);
+          if (split) {
+            dvacc[mb] = mfma32(at, pack8(ph), dvacc[mb]);
+            dkacc[mb] = mfma32(aq, pack8(dh), dkacc[mb]);
+          }
+        }
+      }
+    }
+
+    if (t + 1 < ntiles) store_tile(b ^ 1);
+    __syncthreads();
+  }
+
+  if (!key_valid) return;
+  const size_t obase = (static_cast<size_t>(my_key) * hkv + g) * D;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const size_t off = obase + mb * 32 + 8 * gq + 4 * hi;
+      float4* pk = reinterpret_cast<float4*>(dk + off);
+      float4* pv = reinterpret_cast<float4*>(dv + off);
+      float4 a = *pk, c = *pv;
+      a.x += scale * dkacc[mb][4 * gq + 0];
+      a.y += scale * dkacc[mb][4 * gq + 1];
+      a.z += scale * dkacc[mb][4 * gq + 2];
+      a.w += scale * dkacc[mb][4 * gq + 3];
+      c.x += dvacc[mb][4 * gq + 0];
+      c.y += dvacc[mb][4 * gq + 1];
+      c.z += dvacc[mb][4 * gq + 2];
+      c.w += dvacc[mb][4 * gq + 3];
+      *pk = a;
+      *pv = c;
+    }
+}
+
+template <int D, int G>
+static void main_bwd_mfma_dg(const MainArgs& a) {
+  {
+    constexpr int TPB = bwdq::NW * (32 / G);
+    const int nblk_tok = (a.nq + TPB - 1) / TPB;
+    hipLaunchKernelGGL((main_bwd_dq_kernel<D, G>), dim3(nblk_tok * a.hkv), dim3(512), 0, a.stream,
+                       static_cast<const uint16_t*>(a.q), a.q_seq, a.q_pos, a.nq,
+                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                       a.k_seq, a.k_pos, a.nk, a.hq, a.hkv, a.scale,
+                       static_cast<const uint16_t*>(a.dout), a.lse, a.delta, a.dq);
+  }
+  {
+    const int nblk = (a.nk + bwdkv::KB - 1) / bwdkv::KB;
+    hipLaunchKernelGGL((main_bwd_dkdv_kernel<D, G>), dim3(nblk * a.hkv), dim3(256), 0, a.stream,
+                       static_cast<const uint16_t*>(a.q), a.q_seq, a.q_pos, a.nq,
+                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                       a.k_seq, a.k_pos, a.nk, a.hq, a.hkv, a.scale,
+                       static_cast<const uint16_t*>(a.dout), a.lse, a.delta, a.dk, a.dv);
+  }
+}
+
+template <int D>
+static void main_bwd_mfma_d(const MainArgs& a) {
+  switch (a.hq / a.hkv) {
+    case 1: main_bwd_mfma_dg<D, 1>(a); break;
+    case 2: main_bwd_mfma_dg<D, 2>(a); break;
+    case 4: main_bwd_mfma_dg<D, 4>(a); break;
+    case 8: main_bwd_mfma_dg<D, 8>(a); break;
+    case 16: main_bwd_mfma_dg<D, 16>(a); break;
+    default: main_bwd_mfma_dg<D, 32>(a); break;
+  }
+}
+
+hipError_t launch_main_bwd_mfma(const MainArgs& a) {
+  if (a.nq == 0 || a.nk == 0) return hipSuccess;
+  if (a.d == 128) main_bwd_mfma_d<128>(a); else main_bwd_mfma_d<64>(a);
+  return hipGetLastError();
+}
+
+}  // namespace bac

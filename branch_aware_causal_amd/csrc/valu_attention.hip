@@ -1,0 +1,454 @@
+// Vector-ALU attention kernels (gfx950, wave64):
+//   * rank-local branch attention, forward and backward ([G] 技术贡献: the
+//     local branch part of a branch query; branch K/V stays on its rank);
+//   * the fp32 main-attention path (one wave per (row, head); fp32 has no
+//     MFMA product worth the packing at the sizes it serves).
+// Branch work is a few keys per row and HBM-bound, so one wave handles one
+// (branch, kv-head) with lanes spread over the head dimension; dot products
+// are wave reductions.  All index reads are range-clamped.
+
+#include <climits>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace bac {
+
+template <typename T, int EPL>
+__device__ __forceinline__ void load_lane(const T* base, size_t off, int lane, float (&x)[EPL]) {
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) x[e] = Elem<T>::load(base, off + lane * EPL + e);
+}
+
+// Normalise a row's running (o, m2, l), optionally merge it into the
+// accumulators, and store.  m2 is the running max in log2 units, l the
+// running sum of exp2(x - m2).
+template <typename T, int EPL>
+__device__ __forceinline__ void finish_row(const float (&o)[EPL], float m2, float l, size_t voff,
+                                           size_t lidx, int mode, float* o_acc, float* lse_acc,
+                                           T* o_out, int lane) {
+  float lse2, inv;
+  if (l > 0.f) {
+    lse2 = m2 + log2_fast(l);
+    inv = 1.f / l;
+  } else {
+    lse2 = kNegInf;
+    inv = 0.f;
+  }
+  float res[EPL];
+  float lnew = lse2;
+  if (mode == 1) {
+    float wa, wb;
+    merge_weights_log2(lse_acc[lidx] * kLog2e, lse2, wa, wb, lnew);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) res[e] = wa * o_acc[voff + lane * EPL + e] + wb * (o[e] * inv);
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) res[e] = o[e] * inv;
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    o_acc[voff + lane * EPL + e] = res[e];
+    if (o_out) Elem<T>::store(o_out, voff + lane * EPL + e, res[e]);
+  }
+  if (lane == 0) lse_acc[lidx] = (lnew == kNegInf) ? kNegInf : lnew * kLn2;
+}
+
+// Compensated (Kahan) accumulation: the fp32 gradients sum up to thousands
+// of terms per element, and plain sequential fp32 sums lose ~sqrt(n) ulps.
+__device__ __forceinline__ void kahan_add(float& sum, float& comp, float x) {
+  const float y = x - comp;
+  const float t = sum + y;
+  comp = (t - sum) - y;
+  sum = t;
+}
+
+// Online-softmax update with one key's score x (log2 units) and value v.
+template <int EPL>
+__device__ __forceinline__ void online_update(float x, const float (&v)[EPL], float& m2, float& l,
+                                              float (&o)[EPL]) {
+  const float mn = fmaxf(m2, x);
+  const float corr = exp2_fast(m2 - mn);   // m2 = -inf -> 0
+  const float p = exp2_fast(x - mn);
+  l = l * corr + p;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = o[e] * corr + p * v[e];
+  m2 = mn;
+}
+
+// ---------------------------------------------------------------------------
+// Branch forward: wave w of block b handles branch a = 4b + w, kv-head
+// blockIdx.y, i.e. rows (t, h) for every token t of the branch and every
+// q-head h of the group.  Any branch length is handled (no LDS).
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void branch_fwd_kernel(const T* __restrict__ qb,
+                                                         const T* __restrict__ kb,
+                                                         const T* __restrict__ vb, int nb,
+                                                         const int32_t* __restrict__ bcu, int A,
+                                                         int bidir, int hq, int hkv,
+                                                         float scale_log2, float* o_acc,
+                                                         float* lse_acc, int mode, T* o_out) {
+  constexpr int EPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int a = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (a >= A) return;
+  const int g = blockIdx.y;
+  const int G = hq / hkv;
+  const int t0 = max(0, min(bcu[a], nb));
+  const int t1 = max(t0, min(bcu[a + 1], nb));
+  const int len = t1 - t0;
+  for (int t = 0; t < len; ++t) {
+    const int kend = bidir ? len : t + 1;
+    for (int hl = 0; hl < G; ++hl) {
+      const int h = g * G + hl;
+      const size_t qoff = (static_cast<size_t>(t0 + t) * hq + h) * D;
+      float q[EPL], o[EPL];
+      load_lane<T, EPL>(qb, qoff, lane, q);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+      float m2 = kNegInf, l = 0.f;
+      for (int u = 0; u < kend; ++u) {
+        const size_t koff = (static_cast<size_t>(t0 + u) * hkv + g) * D;
+        float kk[EPL], vv[EPL];
+        load_lane<T, EPL>(kb, koff, lane, kk);
+        load_lane<T, EPL>(vb, koff, lane, vv);
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dot += q[e] * kk[e];
+        dot = wave_sum(dot);
+        online_update<EPL>(dot * scale_log2, vv, m2, l, o);
+      }
+      finish_row<T, EPL>(o, m2, l, qoff, static_cast<size_t>(h) * nb + t0 + t, mode, o_acc,
+                         lse_acc, o_out, lane);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Branch backward: one wave per (branch, kv-head).  For each row (t, h) and
+// each visible key u: s, P = exp2(s*c - lse2), dP = <dO, v_u>,
+// dS = P (dP - Delta); dq_row += dS k_u (registers), dk_u += dS q_row and
+// dv_u += P dO_row (LDS, lane-private slots, so no atomics).  The wave owns
+// every row and key it touches, so += on the global accumulators is race-free.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(64) void branch_bwd_kernel(
+    const T* __restrict__ qb, const T* __restrict__ kb, const T* __restrict__ vb, int nb,
+    const int32_t* __restrict__ bcu, int A, int max_len, int bidir, int hq, int hkv, float scale,
+    const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    float* dq, float* dk, float* dv) {
+  constexpr int EPL = D / 64;
+  extern __shared__ float smem[];
+  float* dk_s = smem;                   // [max_len][D]
+  float* dv_s = smem + max_len * D;     // [max_len][D]
+  const int lane = threadIdx.x;
+  const int a = blockIdx.x;
+  if (a >= A) return;
+  const int g = blockIdx.y;
+  const int G = hq / hkv;
+  const float scale_log2 = scale * kLog2e;
+  const int t0 = max(0, min(bcu[a], nb));
+  const int t1 = max(t0, min(bcu[a + 1], nb));
+  const int len = min(t1 - t0, max_len);
+  for (int u = 0; u < len; ++u)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      dk_s[u * D + lane * EPL + e] = 0.f;
+      dv_s[u * D + lane * EPL + e] = 0.f;
+    }
+  for (int t = 0; t < len; ++t) {
+    const int kend = bidir ? len : t + 1;
+    for (int hl = 0; hl < G; ++hl) {
+      const int h = g * G + hl;
+      const size_t qoff = (static_cast<size_t>(t0 + t) * hq + h) * D;
+      const size_t li = static_cast<size_t>(h) * nb + t0 + t;
+      float q[EPL], d_o[EPL], dqr[EPL];
+      load_lane<T, EPL>(qb, qoff, lane, q);
+      load_lane<T, EPL>(dout, qoff, lane, d_o);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dqr[e] = 0.f;
+      const float lse2 = lse[li] * kLog2e;
+      const float dl = delta[li];
+      for (int u = 0; u < kend; ++u) {
+        const size_t koff = (static_cast<size_t>(t0 + u) * hkv + g) * D;
+        float kk[EPL], vv[EPL];
+        load_lane<T, EPL>(kb, koff, lane, kk);
+        load_lane<T, EPL>(vb, koff, lane, vv);
+        float s = 0.f, dp = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          s += q[e] * kk[e];
+          dp += d_o[e] * vv[e];
+        }
+        s = wave_sum(s);
+        dp = wave_sum(dp);
+        const float p = (lse2 == kNegInf) ? 0.f : exp2_fast(s * scale_log2 - lse2);
+        const float ds = p * (dp - dl);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          dqr[e] += ds * kk[e];
+          dk_s[u * D + lane * EPL + e] += ds * q[e];
+          dv_s[u * D + lane * EPL + e] += p * d_o[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dq[qoff + lane * EPL + e] += scale * dqr[e];
+    }
+  }
+  for (int u = 0; u < len; ++u) {
+    const size_t koff = (static_cast<size_t>(t0 + u) * hkv + g) * D;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      dk[koff + lane * EPL + e] += scale * dk_s[u * D + lane * EPL + e];
+      dv[koff + lane * EPL + e] += dv_s[u * D + lane * EPL + e];
+    }
+  }
+}
+
+template <typename T, int D>
+static void branch_fwd_d(const BranchArgs& a) {
+  const dim3 grid((a.num_branches + 3) / 4, a.hkv);
+  hipLaunchKernelGGL((branch_fwd_kernel<T, D>), grid, dim3(256), 0, a.stream,
+                     static_cast<const T*>(a.qb), static_cast<const T*>(a.kb),
+                     static_cast<const T*>(a.vb), a.nb, a.branch_cu, a.num_branches, a.bidir, a.hq,
+                     a.hkv, a.scale * kLog2e, a.o_acc, a.lse_acc, a.mode, static_cast<T*>(a.o_out));
+}
+
+hipError_t launch_branch_fwd(const BranchArgs& a) {
+  if (a.num_branches == 0) return hipSuccess;
+  if (a.dt == kF32) {
+    if (a.d == 128) branch_fwd_d<float, 128>(a); else branch_fwd_d<float, 64>(a);
+  } else {
+    if (a.d == 128) branch_fwd_d<uint16_t, 128>(a); else branch_fwd_d<uint16_t, 64>(a);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static void branch_bwd_d(const BranchArgs& a) {
+  const dim3 grid(a.num_branches, a.hkv);
+  const size_t lds = branch_bwd_lds_bytes(a.max_len, D);
+  hipLaunchKernelGGL((branch_bwd_kernel<T, D>), grid, dim3(64), lds, a.stream,
+                     static_cast<const T*>(a.qb), static_cast<const T*>(a.kb),
+                     static_cast<const T*>(a.vb), a.nb, a.branch_cu, a.num_branches, a.max_len,
+                     a.bidir, a.hq, a.hkv, a.scale, static_cast<const T*>(a.dout), a.lse, a.delta,
+                     a.dq, a.dk, a.dv);
+}
+
+hipError_t launch_branch_bwd(const BranchArgs& a) {
+  if (a.num_branches == 0) return hipSuccess;
+  if (a.dt == kF32) {
+    if (a.d == 128) branch_bwd_d<float, 128>(a); else branch_bwd_d<float, 64>(a);
+  } else {
+    if (a.d == 128) branch_bwd_d<uint16_t, 128>(a); else branch_bwd_d<uint16_t, 64>(a);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Main attention on vector ALUs: one wave per (query row, q-head).  Keys of
+// the row's sequence with pos <= the row's pos form one contiguous range of
+// the (seq, pos)-sorted shard, found by binary search.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void main_fwd_valu_kernel(
+    const T* __restrict__ q, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
+    int nq, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ k_seq,
+    const int32_t* __restrict__ k_pos, int nk, int hq, int hkv, float scale_log2, float* o_acc,
+    float* lse_acc, int mode, T* o_out) {
+  constexpr int EPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (w >= static_cast<int64_t>(nq) * hq) return;
+  const int i = static_cast<int>(w / hq);
+  const int h = static_cast<int>(w % hq);
+  const int g = h / (hq / hkv);
+  const int s = q_seq[i], p = q_pos[i];
+  const int lo = lower_bound_sp(k_seq, k_pos, nk, s, INT_MIN);
+  const int hi = upper_bound_sp(k_seq, k_pos, nk, s, p);
+  const size_t qoff = (static_cast<size_t>(i) * hq + h) * D;
+  float qq[EPL], o[EPL];
+  load_lane<T, EPL>(q, qoff, lane, qq);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+  float m2 = kNegInf, l = 0.f;
+  for (int j = lo; j < hi; ++j) {
+    if (k_seq[j] != s || k_pos[j] > p) continue;
+    const size_t koff = (static_cast<size_t>(j) * hkv + g) * D;
+    float kk[EPL], vv[EPL];
+    load_lane<T, EPL>(k, koff, lane, kk);
+    load_lane<T, EPL>(v, koff, lane, vv);
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dot += qq[e] * kk[e];
+    dot = wave_sum(dot);
+    online_update<EPL>(dot * scale_log2, vv, m2, l, o);
+  }
+  finish_row<T, EPL>(o, m2, l, qoff, static_cast<size_t>(h) * nq + i, mode, o_acc, lse_acc, o_out,
+                     lane);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void main_bwd_dq_valu_kernel(
+    const T* __restrict__ q, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
+    int nq, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ k_seq,
+    const int32_t* __restrict__ k_pos, int nk, int hq, int hkv, float scale,
+    const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    float* dq) {
+  constexpr int EPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (w >= static_cast<int64_t>(nq) * hq) return;
+  const int i = static_cast<int>(w / hq);
+  const int h = static_cast<int>(w % hq);
+  const int g = h / (hq / hkv);
+  const int s = q_seq[i], p = q_pos[i];
+  const int lo = lower_bound_sp(k_seq, k_pos, nk, s, INT_MIN);
+  const int hi = upper_bound_sp(k_seq, k_pos, nk, s, p);
+  const size_t qoff = (static_cast<size_t>(i) * hq + h) * D;
+  const size_t li = static_cast<size_t>(h) * nq + i;
+  const float lse2 = lse[li] * kLog2e;
+  const float dl = delta[li];
+  const float scale_log2 = scale * kLog2e;
+  float qq[EPL], d_o[EPL], acc[EPL], accc[EPL];
+  load_lane<T, EPL>(q, qoff, lane, qq);
+  load_lane<T, EPL>(dout, qoff, lane, d_o);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = accc[e] = 0.f;
+  if (lse2 != kNegInf) {
+    for (int j = lo; j < hi; ++j) {
+      if (k_seq[j] != s || k_pos[j] > p) continue;
+      const size_t koff = (static_cast<size_t>(j) * hkv + g) * D;
+      float kk[EPL], vv[EPL];
+      load_lane<T, EPL>(k, koff, lane, kk);
+      load_lane<T, EPL>(v, koff, lane, vv);
+      float sc = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        sc += qq[e] * kk[e];
+        dp += d_o[e] * vv[e];
+      }
+      sc = wave_sum(sc);
+      dp = wave_sum(dp);
+      const float pr = exp2_fast(sc * scale_log2 - lse2);
+      const float ds = pr * (dp - dl);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) kahan_add(acc[e], accc[e], ds * kk[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) dq[qoff + lane * EPL + e] += scale * (acc[e] - accc[e]);
+}
+
+// One wave per (key, kv-head): rows of the key's sequence with pos >= the
+// key's pos form one contiguous range of the sorted query rows.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void main_bwd_dkdv_valu_kernel(
+    const T* __restrict__ q, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
+    int nq, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ k_seq,
+    const int32_t* __restrict__ k_pos, int nk, int hq, int hkv, float scale,
+    const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    float* dk, float* dv) {
+  constexpr int EPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (w >= static_cast<int64_t>(nk) * hkv) return;
+  const int j = static_cast<int>(w / hkv);
+  const int g = static_cast<int>(w % hkv);
+  const int G = hq / hkv;
+  const int s = k_seq[j], p = k_pos[j];
+  const int lo = lower_bound_sp(q_seq, q_pos, nq, s, p);
+  const int hi = upper_bound_sp(q_seq, q_pos, nq, s, INT_MAX);
+  const size_t koff = (static_cast<size_t>(j) * hkv + g) * D;
+  const float scale_log2 = scale * kLog2e;
+  float kk[EPL], vv[EPL], dka[EPL], dva[EPL], dkc[EPL], dvc[EPL];
+  load_lane<T, EPL>(k, koff, lane, kk);
+  load_lane<T, EPL>(v, koff, lane, vv);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) dka[e] = dva[e] = dkc[e] = dvc[e] = 0.f;
+  for (int i = lo; i < hi; ++i) {
+    if (q_seq[i] != s || q_pos[i] < p) continue;
+    for (int hl = 0; hl < G; ++hl) {
+      const int h = g * G + hl;
+      const size_t qoff = (static_cast<size_t>(i) * hq + h) * D;
+      const size_t li = static_cast<size_t>(h) * nq + i;
+      const float lse2 = lse[li] * kLog2e;
+      if (lse2 == kNegInf) continue;
+      float qq[EPL], d_o[EPL];
+      load_lane<T, EPL>(q, qoff, lane, qq);
+      load_lane<T, EPL>(dout, qoff, lane, d_o);
+      float sc = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        sc += qq[e] * kk[e];
+        dp += d_o[e] * vv[e];
+      }
+      sc = wave_sum(sc);
+      dp = wave_sum(dp);
+      const float pr = exp2_fast(sc * scale_log2 - lse2);
+      const float ds = pr * (dp - delta[li]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        kahan_add(dka[e], dkc[e], ds * qq[e]);
+        kahan_add(dva[e], dvc[e], pr * d_o[e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    dk[koff + lane * EPL + e] += scale * (dka[e] - dkc[e]);
+    dv[koff + lane * EPL + e] += dva[e] - dvc[e];
+  }
+}
+
+template <typename T, int D>
+static void main_fwd_valu_d(const MainArgs& a) {
+  const int64_t waves = static_cast<int64_t>(a.nq) * a.hq;
+  hipLaunchKernelGGL((main_fwd_valu_kernel<T, D>), dim3(static_cast<unsigned>((waves + 3) / 4)),
+                     dim3(256), 0, a.stream, static_cast<const T*>(a.q), a.q_seq, a.q_pos, a.nq,
+                     static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.k_seq, a.k_pos, a.nk,
+                     a.hq, a.hkv, a.scale * kLog2e, a.o_acc, a.lse_acc, a.mode,
+                     static_cast<T*>(a.o_out));
+}
+
+hipError_t launch_main_fwd_valu(const MainArgs& a) {
+  if (a.nq == 0) return hipSuccess;
+  if (a.dt == kF32) {
+    if (a.d == 128) main_fwd_valu_d<float, 128>(a); else main_fwd_valu_d<float, 64>(a);
+  } else {
+    if (a.d == 128) main_fwd_valu_d<uint16_t, 128>(a); else main_fwd_valu_d<uint16_t, 64>(a);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static void main_bwd_valu_d(const MainArgs& a) {
+  const int64_t qw = static_cast<int64_t>(a.nq) * a.hq;
+  if (qw > 0)
+    hipLaunchKernelGGL((main_bwd_dq_valu_kernel<T, D>), dim3(static_cast<unsigned>((qw + 3) / 4)),
+                       dim3(256), 0, a.stream, static_cast<const T*>(a.q), a.q_seq, a.q_pos, a.nq,
+                       static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.k_seq, a.k_pos,
+                       a.nk, a.hq, a.hkv, a.scale, static_cast<const T*>(a.dout), a.lse, a.delta,
+                       a.dq);
+  const int64_t kw = static_cast<int64_t>(a.nk) * a.hkv;
+  if (kw > 0)
+    hipLaunchKernelGGL((main_bwd_dkdv_valu_kernel<T, D>),
+                       dim3(static_cast<unsigned>((kw + 3) / 4)), dim3(256), 0, a.stream,
+                       static_cast<const T*>(a.q), a.q_seq, a.q_pos, a.nq,
+                       static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.k_seq, a.k_pos,
+                       a.nk, a.hq, a.hkv, a.scale, static_cast<const T*>(a.dout), a.lse, a.delta,
+                       a.dk, a.dv);
+}
+
+hipError_t launch_main_bwd_valu(const MainArgs& a) {
+  if (a.nq == 0 || a.nk == 0) return hipSuccess;
+  if (a.dt == kF32) {
+    if (a.d == 128) main_bwd_valu_d<float, 128>(a); else main_bwd_valu_d<float, 64>(a);
+  } else {
+    if (a.d == 128) main_bwd_valu_d<uint16_t, 128>(a); else main_bwd_valu_d<uint16_t, 64>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bac

@@ -1,0 +1,192 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Small and medium problems, compared element by element with the full oracle
+(definition mode): several 64-key tiles, ragged tails, every branch kind,
+GQA ratios 1..8, head dims 64 and 128, fp32 and bf16, zigzag rings.
+Tolerances (max abs): bf16 2e-2 on O and gradients (fp32 accumulators),
+fp32 1e-5, lse 1e-3; masks and indices bit-exact.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from gpu_util import TOL, check_rne, compare_full, host64, inputs, maxdiff, run_path, say  # noqa: E402
+import oracle  # noqa: E402
+from workloads import WORKLOADS, specs  # noqa: E402
+from workloads.gen import make_structure_custom, make_tensors  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import branch_aware_causal_amd  # noqa: F401  (fails loudly if libbac.so is missing)
+
+
+SMALL = {
+    "eagle3_ragged_bf16": specs.small("e", (300, 129, 1, 77), hq=8, hkv=2, d=128, dtype="bf16",
+                                      branch="eagle3", branch_len=3, seed_base=1000),
+    "dflash_bf16": specs.small("f", (256, 100), hq=8, hkv=2, d=128, dtype="bf16", branch="dflash",
+                               branch_len=16, anchor_stride=16, seed_base=1100),
+    "dspark_d64_bf16": specs.small("s", (200, 64, 3), hq=4, hkv=1, d=64, dtype="bf16",
+                                   branch="dspark", branch_len=8, anchor_stride=8, seed_base=1200),
+    "eagle3_gqa1_bf16": specs.small("g1", (150,), hq=4, hkv=4, d=128, dtype="bf16",
+                                    branch="eagle3", branch_len=2, seed_base=1300),
+    "eagle3_gqa8_d64_bf16": specs.small("g8", (97, 40), hq=16, hkv=2, d=64, dtype="bf16",
+                                        branch="eagle3", branch_len=4, seed_base=1400),
+    "eagle3_f32": specs.small("f32", (70, 33), hq=8, hkv=2, d=128, dtype="f32", branch="eagle3",
+                              branch_len=3, seed_base=1500),
+    "dflash_d64_f32": specs.small("f32b", (64, 20), hq=4, hkv=2, d=64, dtype="f32",
+                                  branch="dflash", branch_len=8, anchor_stride=8, seed_base=1600),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_problem_matches_oracle(name):
+    w = SMALL[name]
+    say(f"case {name}: seqs={w.seqlens} hq={w.hq} hkv={w.hkv} d={w.d} {w.dtype} {w.branch}")
+    st, t = inputs(w)
+    gpu = run_path(st, t)
+    compare_full(st, t, gpu, TOL[w.dtype], name)
+    check_rne(gpu)
+
+
+def test_tiny_eagle3_fp32_workload():
+    """Two packed sequences of 96 and 160 tokens, EAGLE-3 TTT depth 3,
+    Hq=4, Hkv=2, d=64, fp32: the whole problem, fp32 tolerance."""
+    w = WORKLOADS["eagle3_tiny_fp32"]
+    st, t = inputs(w)
+    gpu = run_path(st, t)
+    compare_full(st, t, gpu, TOL["f32"], w.name)
+    check_rne(gpu)
+
+
+@pytest.mark.parametrize("cp", [2, 3, 4])
+def test_zigzag_ring_small_matches_oracle(cp):
+    w = SMALL["eagle3_ragged_bf16"]
+    st, t = inputs(w)
+    gpu = run_path(st, t, cp=cp)
+    compare_full(st, t, gpu, TOL["bf16"], f"ring C={cp}")
+
+
+def test_ring_dflash_matches_unsharded():
+    w = SMALL["dflash_bf16"]
+    st, t = inputs(w)
+    a = run_path(st, t, cp=1)
+    b = run_path(st, t, cp=4)
+    for key in a:
+        tol = 1e-3 if key.startswith("lse") else 2e-2
+        assert maxdiff(host64(b[key]), host64(a[key])) <= tol, key
+
+
+@pytest.mark.parametrize("impl", ["bf16", "f32"])
+def test_mask_is_bit_exact_with_one_hot_values(impl):
+    """Q = 0 and V = one-hot(key id): every visible score is equal, so
+    O = (1/|V(q)|) on exactly the visible keys and 0 elsewhere, and
+    lse = ln |V(q)|.  Checked on the hand-written mask fixtures' structures."""
+    import os
+    from test_oracle import GOLDEN_FILES, load_golden
+    for fname in GOLDEN_FILES:
+        spec, mat = load_golden(fname)
+        seqlens = [int(x) for x in spec["seqlens"]]
+        anchors = [int(x) for x in spec["anchors"]]
+        blens = [int(x) for x in spec["branch_lens"]]
+        cu = np.concatenate([[0], np.cumsum(seqlens)])
+        per_seq = [[a - cu[s] for a in anchors if cu[s] <= a < cu[s + 1]] for s in range(len(seqlens))]
+        st = make_structure_custom(seqlens, per_seq, blens, spec["kind"][0])
+        d = 64
+        dt = torch.bfloat16 if impl == "bf16" else torch.float32
+        n = mat.shape[0]
+        N, Nb = st.n_main, st.n_branch_tok
+        eye = torch.eye(n, d, dtype=dt, device="cuda")
+        t = dict(q=torch.zeros(N, 2, d, dtype=dt, device="cuda"),
+                 qb=torch.zeros(Nb, 2, d, dtype=dt, device="cuda"),
+                 k=torch.randn(N, 1, d, device="cuda").to(dt),
+                 kb=torch.randn(Nb, 1, d, device="cuda").to(dt),
+                 v=eye[:N, None, :].contiguous(), vb=eye[N:, None, :].contiguous(),
+                 do=torch.zeros(N, 2, d, dtype=dt, device="cuda"),
+                 dob=torch.zeros(Nb, 2, d, dtype=dt, device="cuda"))
+        gpu = run_path(st, t)
+        O = torch.cat([gpu["o_main_acc"], gpu["o_br_acc"]])[:, 0, :n].cpu().numpy()
+        lse = torch.cat([gpu["lse_main"], gpu["lse_br"]], dim=1)[0].cpu().numpy()
+        assert np.array_equal(O > 0, mat), fname
+        counts = mat.sum(axis=1)
+        assert np.all(np.abs(lse - np.log(counts)) < 1.0 / (2 * counts)), fname
+        assert np.allclose(O[mat], np.repeat(1.0 / counts, counts), rtol=1e-2), fname
+
+
+def test_lse_merge_kernel_matches_oracle_merge():
+    from branch_aware_causal_amd import lse_merge
+    g = torch.Generator(device="cuda").manual_seed(5)
+    n, hq, d = 333, 4, 128
+    oa = torch.randn(n, hq, d, generator=g, device="cuda")
+    ob = torch.randn(n, hq, d, generator=g, device="cuda")
+    la = torch.randn(hq, n, generator=g, device="cuda") * 4
+    lb = torch.randn(hq, n, generator=g, device="cuda") * 4
+    la[0, :50] = -math.inf
+    lb[1, 25:75] = -math.inf
+    la[2, 10:20] = -math.inf
+    lb[2, 10:20] = -math.inf
+    oa[la.T == -math.inf] = 0
+    ob[lb.T == -math.inf] = 0
+    ref_o, ref_l = oracle.lse_merge(host64(oa), host64(la).T, host64(ob), host64(lb).T)
+    o_out = torch.empty(n, hq, d, dtype=torch.bfloat16, device="cuda")
+    lse_merge(oa, la, ob, lb, o_out=o_out)
+    torch.cuda.synchronize()
+    assert maxdiff(host64(oa), ref_o) < 1e-5
+    assert maxdiff(host64(la).T, ref_l) < 1e-5
+    assert torch.equal(oa.to(torch.bfloat16), o_out)
+
+
+def test_delta_kernel():
+    from branch_aware_causal_amd import attn_bwd_delta
+    g = torch.Generator(device="cuda").manual_seed(6)
+    n, hq, d = 129, 8, 64
+    o = torch.randn(n, hq, d, generator=g, device="cuda")
+    do = torch.randn(n, hq, d, generator=g, device="cuda").to(torch.bfloat16)
+    delta = torch.empty(hq, n, device="cuda")
+    attn_bwd_delta(o, do, delta)
+    ref = oracle.delta(host64(o), host64(do)).T
+    assert maxdiff(host64(delta), ref) < 1e-4
+
+
+def test_empty_and_fully_masked_shards():
+    """WRITE over an empty key set or a shard wholly after the rows gives
+    (O = 0, lse = -inf); MERGE of it leaves the accumulators unchanged."""
+    from branch_aware_causal_amd import attn_main_fwd
+    dev = "cuda"
+    nq, hq, hkv, d = 70, 8, 2, 128
+    q = torch.randn(nq, hq, d, device=dev).to(torch.bfloat16)
+    qs = torch.zeros(nq, dtype=torch.int32, device=dev)
+    qp = torch.arange(nq, dtype=torch.int32, device=dev)
+    k = torch.randn(100, hkv, d, device=dev).to(torch.bfloat16)
+    ks = torch.zeros(100, dtype=torch.int32, device=dev)
+    kp = torch.arange(1000, 1100, dtype=torch.int32, device=dev)    # all after the rows
+    o = torch.full((nq, hq, d), 7.0, device=dev)
+    l = torch.full((hq, nq), 3.0, device=dev)
+    attn_main_fwd(q, qs, qp, k, k, ks, kp, o, l, "merge")
+    torch.cuda.synchronize()
+    assert torch.all(o == 7.0) and torch.all(l == 3.0)
+    attn_main_fwd(q, qs, qp, k, k, ks, kp, o, l, "write")
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(l == -math.inf)
+    e = torch.empty(0, hkv, d, dtype=torch.bfloat16, device=dev)
+    ei = torch.empty(0, dtype=torch.int32, device=dev)
+    o.fill_(1.0)
+    attn_main_fwd(q, qs, qp, e, e, ei, ei, o, l, "write")
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(l == -math.inf)
+
+
+def test_check_index_counts_violations():
+    from branch_aware_causal_amd import attn_check_index
+    seq = torch.tensor([0, 0, 0, 1, 1, 0], dtype=torch.int32, device="cuda")
+    pos = torch.tensor([0, 1, 1, 0, -3, 5], dtype=torch.int32, device="cuda")
+    assert attn_check_index(seq, pos, strict=False) == 2   # (1,-3): pos<0 and order; (0,5)<(1,-3)
+    assert attn_check_index(seq, pos, strict=True) == 3    # plus the repeated (0,1)
