@@ -41,6 +41,10 @@ SIGNATURES = {
     "attn_bwd_delta": [vp, i32, vp, i32, i32, i32, i32, vp, vp],
     "attn_main_bwd": [vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                       vp, vp, vp, vp, vp, vp, vp],
+    "attn_main_bwd_dq": [vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                         vp, vp, vp, vp, vp],
+    "attn_main_bwd_dkdv": [vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                           vp, vp, vp, vp, vp, vp],
     "attn_branch_bwd": [vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32,
                         vp, vp, vp, vp, vp, vp, vp],
     "attn_check_index": [vp, vp, i32, i32, vp, vp],

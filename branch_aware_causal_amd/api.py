@@ -174,13 +174,11 @@ def attn_bwd_delta(o, dout, delta, stream=None):
     _check(st)
 
 
-def attn_main_bwd(q, q_seq, q_pos, k, v, k_seq, k_pos, dout, lse, delta, dq, dk, dv, scale=None,
-                  stream=None):
+def _main_bwd_args(q, q_seq, q_pos, k, v, k_seq, k_pos, dout, lse, delta, dq, dk, dv):
     nq, hq, d = q.shape
     nk, hkv = k.shape[0], k.shape[1]
     torch = _torch()
     _need(q, "q")
-    dt = _dt(q)
     _need(k, "k", q.dtype, (nk, hkv, d))
     _need(v, "v", q.dtype, (nk, hkv, d))
     for t, nm, n in ((q_seq, "q_seq", nq), (q_pos, "q_pos", nq), (k_seq, "k_seq", nk),
@@ -189,13 +187,44 @@ def attn_main_bwd(q, q_seq, q_pos, k, v, k_seq, k_pos, dout, lse, delta, dq, dk,
     _need(dout, "dout", q.dtype, (nq, hq, d))
     _need(lse, "lse", torch.float32, (hq, nq))
     _need(delta, "delta", torch.float32, (hq, nq))
-    _need(dq, "dq", torch.float32, (nq, hq, d))
-    _need(dk, "dk", torch.float32, (nk, hkv, d))
-    _need(dv, "dv", torch.float32, (nk, hkv, d))
+    if dq is not None:
+        _need(dq, "dq", torch.float32, (nq, hq, d))
+    if dk is not None:
+        _need(dk, "dk", torch.float32, (nk, hkv, d))
+        _need(dv, "dv", torch.float32, (nk, hkv, d))
+    return nq, hq, d, nk, hkv, _dt(q)
+
+
+def attn_main_bwd(q, q_seq, q_pos, k, v, k_seq, k_pos, dout, lse, delta, dq, dk, dv, scale=None,
+                  stream=None):
+    nq, hq, d, nk, hkv, dt = _main_bwd_args(q, q_seq, q_pos, k, v, k_seq, k_pos, dout, lse, delta,
+                                            dq, dk, dv)
     st = _lib.load().attn_main_bwd(_ptr(q), _ptr(q_seq), _ptr(q_pos), nq, _ptr(k), _ptr(v),
                                    _ptr(k_seq), _ptr(k_pos), nk, hq, hkv, d, dt, _scale(scale, d),
                                    _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
                                    _stream(stream))
+    _check(st)
+
+
+def attn_main_bwd_dq(q, q_seq, q_pos, k, v, k_seq, k_pos, dout, lse, delta, dq, scale=None,
+                     stream=None):
+    nq, hq, d, nk, hkv, dt = _main_bwd_args(q, q_seq, q_pos, k, v, k_seq, k_pos, dout, lse, delta,
+                                            dq, None, None)
+    st = _lib.load().attn_main_bwd_dq(_ptr(q), _ptr(q_seq), _ptr(q_pos), nq, _ptr(k), _ptr(v),
+                                      _ptr(k_seq), _ptr(k_pos), nk, hq, hkv, d, dt,
+                                      _scale(scale, d), _ptr(dout), _ptr(lse), _ptr(delta),
+                                      _ptr(dq), _stream(stream))
+    _check(st)
+
+
+def attn_main_bwd_dkdv(q, q_seq, q_pos, k, v, k_seq, k_pos, dout, lse, delta, dk, dv, scale=None,
+                       stream=None):
+    nq, hq, d, nk, hkv, dt = _main_bwd_args(q, q_seq, q_pos, k, v, k_seq, k_pos, dout, lse, delta,
+                                            None, dk, dv)
+    st = _lib.load().attn_main_bwd_dkdv(_ptr(q), _ptr(q_seq), _ptr(q_pos), nq, _ptr(k), _ptr(v),
+                                        _ptr(k_seq), _ptr(k_pos), nk, hq, hkv, d, dt,
+                                        _scale(scale, d), _ptr(dout), _ptr(lse), _ptr(delta),
+                                        _ptr(dk), _ptr(dv), _stream(stream))
     _check(st)
 
 

@@ -184,17 +184,19 @@ bac_status attn_bwd_delta(const void* o, bac_dtype o_dt, const void* dout, bac_d
                     fn);
 }
 
-bac_status attn_main_bwd(const void* q, const int32_t* q_seq, const int32_t* q_pos, int32_t nq,
-                         const void* k, const void* v, const int32_t* k_seq, const int32_t* k_pos,
-                         int32_t nk, int32_t hq, int32_t hkv, int32_t d, bac_dtype dt, float scale,
-                         const void* dout, const float* lse, const float* delta, float* dq_acc,
-                         float* dk_acc, float* dv_acc, void* stream) {
-  clear_error();
-  const char* fn = "attn_main_bwd";
+// part: 0 = whole backward, 1 = dq only, 2 = dk/dv only.
+static bac_status main_bwd_impl(const char* fn, int part, const void* q, const int32_t* q_seq,
+                                const int32_t* q_pos, int32_t nq, const void* k, const void* v,
+                                const int32_t* k_seq, const int32_t* k_pos, int32_t nk, int32_t hq,
+                                int32_t hkv, int32_t d, int32_t dt, float scale, const void* dout,
+                                const float* lse, const float* delta, float* dq_acc, float* dk_acc,
+                                float* dv_acc, void* stream) {
   BAC_TRY(check_main(fn, q, q_seq, q_pos, nq, k, v, k_seq, k_pos, nk, hq, hkv, d, dt, scale));
-  if (nq > 0 && (!dout || !lse || !delta || !dq_acc))
-    return fail(BAC_EINVAL, "%s: null dout, lse, delta or dq_acc", fn);
-  if (nk > 0 && (!dk_acc || !dv_acc)) return fail(BAC_EINVAL, "%s: null dk_acc or dv_acc", fn);
+  if (nq > 0 && (!dout || !lse || !delta))
+    return fail(BAC_EINVAL, "%s: null dout, lse or delta", fn);
+  if (nq > 0 && part != 2 && !dq_acc) return fail(BAC_EINVAL, "%s: null dq_acc", fn);
+  if (nk > 0 && part != 1 && (!dk_acc || !dv_acc))
+    return fail(BAC_EINVAL, "%s: null dk_acc or dv_acc", fn);
   if (nq == 0 || nk == 0) return BAC_OK;
   MainArgs a{};
   a.q = q; a.q_seq = q_seq; a.q_pos = q_pos; a.nq = nq;
@@ -202,8 +204,38 @@ bac_status attn_main_bwd(const void* q, const int32_t* q_seq, const int32_t* q_p
   a.hq = hq; a.hkv = hkv; a.d = d; a.dt = dt; a.scale = scale;
   a.dout = dout; a.lse = lse; a.delta = delta; a.dq = dq_acc; a.dk = dk_acc; a.dv = dv_acc;
   a.stream = static_cast<hipStream_t>(stream);
-  hipError_t e = main_uses_valu(dt) ? launch_main_bwd_valu(a) : launch_main_bwd_mfma(a);
+  hipError_t e = main_uses_valu(dt) ? launch_main_bwd_valu(a, part) : launch_main_bwd_mfma(a, part);
   return hip_status(e, fn);
+}
+
+bac_status attn_main_bwd(const void* q, const int32_t* q_seq, const int32_t* q_pos, int32_t nq,
+                         const void* k, const void* v, const int32_t* k_seq, const int32_t* k_pos,
+                         int32_t nk, int32_t hq, int32_t hkv, int32_t d, bac_dtype dt, float scale,
+                         const void* dout, const float* lse, const float* delta, float* dq_acc,
+                         float* dk_acc, float* dv_acc, void* stream) {
+  clear_error();
+  return main_bwd_impl("attn_main_bwd", 0, q, q_seq, q_pos, nq, k, v, k_seq, k_pos, nk, hq, hkv,
+                       d, dt, scale, dout, lse, delta, dq_acc, dk_acc, dv_acc, stream);
+}
+
+bac_status attn_main_bwd_dq(const void* q, const int32_t* q_seq, const int32_t* q_pos, int32_t nq,
+                            const void* k, const void* v, const int32_t* k_seq,
+                            const int32_t* k_pos, int32_t nk, int32_t hq, int32_t hkv, int32_t d,
+                            bac_dtype dt, float scale, const void* dout, const float* lse,
+                            const float* delta, float* dq_acc, void* stream) {
+  clear_error();
+  return main_bwd_impl("attn_main_bwd_dq", 1, q, q_seq, q_pos, nq, k, v, k_seq, k_pos, nk, hq,
+                       hkv, d, dt, scale, dout, lse, delta, dq_acc, nullptr, nullptr, stream);
+}
+
+bac_status attn_main_bwd_dkdv(const void* q, const int32_t* q_seq, const int32_t* q_pos,
+                              int32_t nq, const void* k, const void* v, const int32_t* k_seq,
+                              const int32_t* k_pos, int32_t nk, int32_t hq, int32_t hkv, int32_t d,
+                              bac_dtype dt, float scale, const void* dout, const float* lse,
+                              const float* delta, float* dk_acc, float* dv_acc, void* stream) {
+  clear_error();
+  return main_bwd_impl("attn_main_bwd_dkdv", 2, q, q_seq, q_pos, nq, k, v, k_seq, k_pos, nk, hq,
+                       hkv, d, dt, scale, dout, lse, delta, nullptr, dk_acc, dv_acc, stream);
 }
 
 bac_status attn_branch_bwd(const void* qb, const void* kb, const void* vb, int32_t nb,

@@ -64,9 +64,10 @@ struct BranchArgs {
 };
 
 hipError_t launch_main_fwd_valu(const MainArgs& a);
-hipError_t launch_main_bwd_valu(const MainArgs& a);
+hipError_t launch_main_bwd_valu(const MainArgs& a, int part = 0);
 hipError_t launch_main_fwd_mfma(const MainArgs& a);
-hipError_t launch_main_bwd_mfma(const MainArgs& a);
+// part: 0 = dq and dk/dv, 1 = dq only, 2 = dk/dv only
+hipError_t launch_main_bwd_mfma(const MainArgs& a, int part = 0);
 hipError_t launch_branch_fwd(const BranchArgs& a);
 hipError_t launch_branch_bwd(const BranchArgs& a);
 hipError_t launch_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,

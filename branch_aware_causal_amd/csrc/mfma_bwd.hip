@@ -475,8 +475,8 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
 }
 
 template <int D, int G>
-static void main_bwd_mfma_dg(const MainArgs& a) {
-  {
+static void main_bwd_mfma_dg(const MainArgs& a, int part) {
+  if (part != 2) {
     constexpr int TPB = bwdq::NW * (32 / G);
     const int nblk_tok = (a.nq + TPB - 1) / TPB;
     hipLaunchKernelGGL((main_bwd_dq_kernel<D, G>), dim3(nblk_tok * a.hkv), dim3(512), 0, a.stream,
@@ -485,7 +485,7 @@ static void main_bwd_mfma_dg(const MainArgs& a) {
                        a.k_seq, a.k_pos, a.nk, a.hq, a.hkv, a.scale,
                        static_cast<const uint16_t*>(a.dout), a.lse, a.delta, a.dq);
   }
-  {
+  if (part != 1) {
     const int nblk = (a.nk + bwdkv::KB - 1) / bwdkv::KB;
     hipLaunchKernelGGL((main_bwd_dkdv_kernel<D, G>), dim3(nblk * a.hkv), dim3(256), 0, a.stream,
                        static_cast<const uint16_t*>(a.q), a.q_seq, a.q_pos, a.nq,
@@ -496,20 +496,20 @@ static void main_bwd_mfma_dg(const MainArgs& a) {
 }
 
 template <int D>
-static void main_bwd_mfma_d(const MainArgs& a) {
+static void main_bwd_mfma_d(const MainArgs& a, int part) {
   switch (a.hq / a.hkv) {
-    case 1: main_bwd_mfma_dg<D, 1>(a); break;
-    case 2: main_bwd_mfma_dg<D, 2>(a); break;
-    case 4: main_bwd_mfma_dg<D, 4>(a); break;
-    case 8: main_bwd_mfma_dg<D, 8>(a); break;
-    case 16: main_bwd_mfma_dg<D, 16>(a); break;
-    default: main_bwd_mfma_dg<D, 32>(a); break;
+    case 1: main_bwd_mfma_dg<D, 1>(a, part); break;
+    case 2: main_bwd_mfma_dg<D, 2>(a, part); break;
+    case 4: main_bwd_mfma_dg<D, 4>(a, part); break;
+    case 8: main_bwd_mfma_dg<D, 8>(a, part); break;
+    case 16: main_bwd_mfma_dg<D, 16>(a, part); break;
+    default: main_bwd_mfma_dg<D, 32>(a, part); break;
   }
 }
 
-hipError_t launch_main_bwd_mfma(const MainArgs& a) {
+hipError_t launch_main_bwd_mfma(const MainArgs& a, int part) {
   if (a.nq == 0 || a.nk == 0) return hipSuccess;
-  if (a.d == 128) main_bwd_mfma_d<128>(a); else main_bwd_mfma_d<64>(a);
+  if (a.d == 128) main_bwd_mfma_d<128>(a, part); else main_bwd_mfma_d<64>(a, part);
   return hipGetLastError();
 }
 

@@ -423,16 +423,16 @@ hipError_t launch_main_fwd_valu(const MainArgs& a) {
 }
 
 template <typename T, int D>
-static void main_bwd_valu_d(const MainArgs& a) {
+static void main_bwd_valu_d(const MainArgs& a, int part) {
   const int64_t qw = static_cast<int64_t>(a.nq) * a.hq;
-  if (qw > 0)
+  if (qw > 0 && part != 2)
     hipLaunchKernelGGL((main_bwd_dq_valu_kernel<T, D>), dim3(static_cast<unsigned>((qw + 3) / 4)),
                        dim3(256), 0, a.stream, static_cast<const T*>(a.q), a.q_seq, a.q_pos, a.nq,
                        static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.k_seq, a.k_pos,
                        a.nk, a.hq, a.hkv, a.scale, static_cast<const T*>(a.dout), a.lse, a.delta,
                        a.dq);
   const int64_t kw = static_cast<int64_t>(a.nk) * a.hkv;
-  if (kw > 0)
+  if (kw > 0 && part != 1)
     hipLaunchKernelGGL((main_bwd_dkdv_valu_kernel<T, D>),
                        dim3(static_cast<unsigned>((kw + 3) / 4)), dim3(256), 0, a.stream,
                        static_cast<const T*>(a.q), a.q_seq, a.q_pos, a.nq,
@@ -441,12 +441,13 @@ static void main_bwd_valu_d(const MainArgs& a) {
                        a.dk, a.dv);
 }
 
-hipError_t launch_main_bwd_valu(const MainArgs& a) {
+hipError_t launch_main_bwd_valu(const MainArgs& a, int part) {
   if (a.nq == 0 || a.nk == 0) return hipSuccess;
   if (a.dt == kF32) {
-    if (a.d == 128) main_bwd_valu_d<float, 128>(a); else main_bwd_valu_d<float, 64>(a);
+    if (a.d == 128) main_bwd_valu_d<float, 128>(a, part); else main_bwd_valu_d<float, 64>(a, part);
   } else {
-    if (a.d == 128) main_bwd_valu_d<uint16_t, 128>(a); else main_bwd_valu_d<uint16_t, 64>(a);
+    if (a.d == 128) main_bwd_valu_d<uint16_t, 128>(a, part);
+    else main_bwd_valu_d<uint16_t, 64>(a, part);
   }
   return hipGetLastError();
 }

@@ -207,6 +207,22 @@ bac_status attn_main_bwd(const void* q, const int32_t* q_seq, const int32_t* q_p
                          const void* dout, const float* lse, const float* delta,
                          float* dq_acc, float* dk_acc, float* dv_acc, void* stream);
 
+/* attn_main_bwd_dq / attn_main_bwd_dkdv -- the two halves of attn_main_bwd,
+ * each a single kernel launch: the first adds to dq_acc only, the second to
+ * dk_acc / dv_acc only.  Same arguments and preconditions as attn_main_bwd
+ * (unused accumulator pointers may be NULL).  For callers that overlap the
+ * dK/dV return of a ring step with the dQ work, or time the two apart. */
+bac_status attn_main_bwd_dq(const void* q, const int32_t* q_seq, const int32_t* q_pos, int32_t nq,
+                            const void* k, const void* v, const int32_t* k_seq,
+                            const int32_t* k_pos, int32_t nk, int32_t hq, int32_t hkv, int32_t d,
+                            bac_dtype dt, float scale, const void* dout, const float* lse,
+                            const float* delta, float* dq_acc, void* stream);
+bac_status attn_main_bwd_dkdv(const void* q, const int32_t* q_seq, const int32_t* q_pos,
+                              int32_t nq, const void* k, const void* v, const int32_t* k_seq,
+                              const int32_t* k_pos, int32_t nk, int32_t hq, int32_t hkv, int32_t d,
+                              bac_dtype dt, float scale, const void* dout, const float* lse,
+                              const float* delta, float* dk_acc, float* dv_acc, void* stream);
+
 /* ------------------------------------------------------------------------
  * attn_branch_bwd -- gradients of attn_branch_fwd's rows over their own
  * branch keys, from the merged lse/delta of those rows.  Arguments as
