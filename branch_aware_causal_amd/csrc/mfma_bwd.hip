@@ -28,7 +28,6 @@ namespace bac {
 namespace bwdq {
 constexpr int BN = 64;
 constexpr int NW = 8;
-constexpr int PAD = 8;
 }  // namespace bwdq
 
 template <int D, int G>
@@ -44,16 +43,14 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
   constexpr int TPB = NW * TPW;
   constexpr int KS = D / 16;
   constexpr int MB = D / 32;
-  constexpr int KROW = D + PAD;
-  constexpr int TROW = BN + PAD;
   constexpr int CPR = D / 8;
   constexpr int LOADS = BN * CPR / 512;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KROW];   // keys (perm rows) x d
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * KROW];   // keys (perm rows) x d
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][D * TROW];    // d x keys
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * D];   // keys x d, swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * D];
   __shared__ __attribute__((aligned(16))) int kseq_s[2][BN];
   __shared__ __attribute__((aligned(16))) int kpos_s[2][BN];
+  __shared__ __attribute__((aligned(16))) uint16_t dOs[NW][32 * D];  // each wave's dO rows
 
   const float scale_log2 = scale * kLog2e;
   const int nblk_tok = (nq + TPB - 1) / TPB;
@@ -64,6 +61,7 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, hi = lane >> 5;
+  const LaneOffsets<D> lo_off(lane);
 
   const int wtok0 = tok0 + wave * TPW;
   const int my_tok = wtok0 + n / G;
@@ -75,6 +73,7 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
   const float my_lse2 = row_valid ? lse[li] * kLog2e : kNegInf;
   const float my_delta = row_valid ? delta[li] : 0.f;
   const bool row_live = row_valid && my_lse2 != kNegInf;
+  const float lse_use = row_live ? my_lse2 : 0.f;
 
   const int wlast = min(nq, wtok0 + TPW) - 1;
   const bool wave_valid = wtok0 < nq;
@@ -87,13 +86,17 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
   const int hi_k = upper_bound_sp(k_seq, k_pos, nk, q_seq[blast], q_pos[blast]);
   const int ntiles = hi_k > lo ? (hi_k - lo + BN - 1) / BN : 0;
 
-  bf16x8 qreg[KS], doreg[KS];
+  // Q operands stay in registers; the wave's dO rows go to LDS (read back as
+  // the B operand of dP^T = V dO^T) to keep the wave within 256 registers.
+  bf16x8 qreg[KS];
+  uint16_t* my_do = dOs[wave];
   {
     const size_t off = (static_cast<size_t>(my_tok) * hq + my_head) * D + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qreg[ks] = row_valid ? *reinterpret_cast<const bf16x8*>(q + off + 16 * ks) : zero8();
-      doreg[ks] = row_valid ? *reinterpret_cast<const bf16x8*>(dout + off + 16 * ks) : zero8();
+      const bf16x8 dv = row_valid ? *reinterpret_cast<const bf16x8*>(dout + off + 16 * ks) : zero8();
+      *reinterpret_cast<bf16x8*>(my_do + lo_off.row[ks]) = dv;
     }
   }
   f32x16 dqacc[MB];
@@ -129,12 +132,8 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
     for (int it = 0; it < LOADS; ++it) {
       const int c = tid + 512 * it;
       const int key = c / CPR, col = (c % CPR) * 8;
-      *reinterpret_cast<uint4*>(&Ks[b][perm_row(key) * KROW + col]) = kreg[it];
-      *reinterpret_cast<uint4*>(&Vs[b][perm_row(key) * KROW + col]) = vreg[it];
-      const uint32_t w[4] = {kreg[it].x, kreg[it].y, kreg[it].z, kreg[it].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        Kt[b][(col + e) * TROW + key] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+      *reinterpret_cast<uint4*>(&Ks[b][toff<D>(key, col)]) = kreg[it];
+      *reinterpret_cast<uint4*>(&Vs[b][toff<D>(key, col)]) = vreg[it];
     }
     if (tid < BN) {
       kseq_s[b][tid] = sreg;
@@ -164,41 +163,41 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
     if (wave_any) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        // S^T = K Q^T and dP^T = V dO^T: lane (n, hi) register r holds key
+        // kb*32 + acc_row(r, hi) of query row n
         f32x16 sacc = zero16(), dpacc = zero16();
-        const uint16_t* kp = &Ks[b][(kb * 32 + n) * KROW + 8 * hi];
-        const uint16_t* vp = &Vs[b][(kb * 32 + n) * KROW + 8 * hi];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          sacc = mfma32(lds_read8(kp + 16 * ks), qreg[ks], sacc);
-          dpacc = mfma32(lds_read8(vp + 16 * ks), doreg[ks], dpacc);
+          sacc = mfma32(row_operand<D>(Ks[b], lo_off, kb * 32, ks), qreg[ks], sacc);
+          dpacc = mfma32(row_operand<D>(Vs[b], lo_off, kb * 32, ks),
+                         row_operand<D>(my_do, lo_off, 0, ks), dpacc);
         }
-        // lane (n, hi) holds keys kb*32 + 16*hi + r of row n
         float ds[16];
-        const int tb0 = kb * 32 + 16 * hi;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          int sv[4] = {0, 0, 0, 0}, pv[4] = {0, 0, 0, 0};
+          int sv[4] = {my_seq, my_seq, my_seq, my_seq}, pv[4] = {0, 0, 0, 0};
           if (!wave_full) {
-            const int4 ss = *reinterpret_cast<const int4*>(&kseq_s[b][tb0 + 4 * r4]);
-            const int4 pp = *reinterpret_cast<const int4*>(&kpos_s[b][tb0 + 4 * r4]);
+            const int t0 = kb * 32 + 8 * r4 + 4 * hi;
+            const int4 ss = *reinterpret_cast<const int4*>(&kseq_s[b][t0]);
+            const int4 pp = *reinterpret_cast<const int4*>(&kpos_s[b][t0]);
             sv[0] = ss.x; sv[1] = ss.y; sv[2] = ss.z; sv[3] = ss.w;
             pv[0] = pp.x; pv[1] = pp.y; pv[2] = pp.z; pv[3] = pp.w;
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * r4 + e;
-            const bool vis = row_live && (wave_full || (sv[e] == my_seq && pv[e] <= my_pos));
-            const float p = vis ? exp2_fast(sacc[r] * scale_log2 - my_lse2) : 0.f;
-            ds[r] = p * (dpacc[r] - my_delta);
+            const bool vis = row_live & (sv[e] == my_seq) & (pv[e] <= my_pos);
+            const float p = exp2_fast(sacc[r] * scale_log2 - lse_use);
+            ds[r] = vis ? p * (dpacc[r] - my_delta) : 0.f;
           }
         }
         // dQ^T += K^T dS^T over the 32 keys of this block (2 k-steps)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const bf16x8 db = pack8(&ds[8 * s2]);
-          const uint16_t* tp = &Kt[b][n * TROW + kb * 32 + 16 * hi + 8 * s2];
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) dqacc[mb] = mfma32(lds_read8(tp + mb * 32 * TROW), db, dqacc[mb]);
+          for (int mb = 0; mb < MB; ++mb)
+            dqacc[mb] = mfma32(tr_operand<D>(Ks[b], lo_off, kb * 32 + 16 * s2, mb), db, dqacc[mb]);
         }
       }
     }
@@ -224,13 +223,13 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV: key-outer.
+// dK / dV: key-outer.  K and V of the workgroup's 128 keys stay in LDS; the
+// query rows that can see them stream through in tiles of 32 rows.
 // ---------------------------------------------------------------------------
 namespace bwdkv {
 constexpr int NW = 4;          // waves per workgroup, 32 keys each
-constexpr float kSplitP = 1.f / 256.f;
 constexpr int KB = NW * 32;    // keys per workgroup
-constexpr int PAD = 8;
+constexpr float kSplitP = 1.f / 256.f;
 }  // namespace bwdkv
 
 template <int D, int G>
@@ -245,15 +244,14 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
   constexpr int TPT = 32 / G;          // tokens per 32-row query tile
   constexpr int KS = D / 16;
   constexpr int MB = D / 32;
-  constexpr int RROW = D + PAD;        // row-major tile stride
-  constexpr int TROW = 32 + PAD;       // transposed tile stride
   constexpr int CPR = D / 8;
-  constexpr int LOADS = 32 * CPR / 256;   // 16-byte chunks per thread per tile (per tensor)
+  constexpr int LOADS = 32 * CPR / 256;     // 16-byte chunks per thread per tile (per tensor)
+  constexpr int KLOADS = KB * CPR / 256;    // chunks per thread for the K / V block
 
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][32 * RROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Ds[2][32 * RROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][D * TROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Dt[2][D * TROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Kw[KB * D];     // keys x d, swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t Vw[KB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][32 * D];  // rows x d, swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t Ds[2][32 * D];
   __shared__ __attribute__((aligned(16))) float lse_s[2][32];
   __shared__ __attribute__((aligned(16))) float dl_s[2][32];
   __shared__ __attribute__((aligned(16))) int rseq_s[2][32];
@@ -268,13 +266,13 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, hi = lane >> 5;
+  const LaneOffsets<D> lo_off(lane);
 
-  // this lane's key
+  // this lane's key (column n of the wave's 32-key block)
   const int my_key = key0 + wave * 32 + n;
   const bool key_valid = my_key < nk;
   const int kseq = key_valid ? k_seq[my_key] : INT_MIN;
   const int kpos = key_valid ? k_pos[my_key] : INT_MAX;
-  // wave-level key summary (keys sorted)
   const int wk0 = key0 + wave * 32;
   const bool wave_valid = wk0 < nk;
   const int wkl = min(nk, wk0 + 32) - 1;
@@ -282,15 +280,20 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
   const int wf_seq = wave_valid ? k_seq[wk0] : 0, wf_pos = wave_valid ? k_pos[wk0] : 0;
   const int wl_seq = wave_valid ? k_seq[wkl] : 0, wl_pos = wave_valid ? k_pos[wkl] : 0;
 
-  // K and V of this lane's key as B operands: key n, d = 16*ks + 8*hi + 0..7
-  bf16x8 kreg[KS], vreg[KS];
-  {
-    const size_t off = (static_cast<size_t>(my_key) * hkv + g) * D + 8 * hi;
+  // K and V of the block into LDS
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kreg[ks] = key_valid ? *reinterpret_cast<const bf16x8*>(k + off + 16 * ks) : zero8();
-      vreg[ks] = key_valid ? *reinterpret_cast<const bf16x8*>(v + off + 16 * ks) : zero8();
+  for (int it = 0; it < KLOADS; ++it) {
+    const int c = tid + 256 * it;
+    const int kr = c / CPR, col = (c % CPR) * 8;
+    const int j = key0 + kr;
+    uint4 kk = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    if (j < nk) {
+      const size_t off = (static_cast<size_t>(j) * hkv + g) * D + col;
+      kk = *reinterpret_cast<const uint4*>(k + off);
+      vv = *reinterpret_cast<const uint4*>(v + off);
     }
+    *reinterpret_cast<uint4*>(&Kw[toff<D>(kr, col)]) = kk;
+    *reinterpret_cast<uint4*>(&Vw[toff<D>(kr, col)]) = vv;
   }
 
   // query tokens that can see any key of the block
@@ -306,24 +309,26 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
     dvacc[mb] = zero16();
   }
 
-  // staging: thread -> (row = tid % 32, chunk = tid / 32 + 8 * it); a row is
-  // (token t0 + row / G, head g*G + row % G)
+  // staging: chunk c -> (row = c / CPR, col); a row is (token t0 + row / G, head g*G + row % G)
   uint4 qr[LOADS], dr[LOADS];
   float lreg = 0.f, dlreg = 0.f;
   int sreg = 0, preg = 0;
   auto load_tile = [&](int t0) {
-    const int row = tid & 31;
-    const int tok = t0 + row / G;
-    const int head = g * G + row % G;
-    const bool ok = tok < qhi;
-    const size_t base = (static_cast<size_t>(tok) * hq + head) * D;
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
-      const int col = ((tid >> 5) + 8 * it) * 8;
-      qr[it] = ok ? *reinterpret_cast<const uint4*>(q + base + col) : make_uint4(0, 0, 0, 0);
-      dr[it] = ok ? *reinterpret_cast<const uint4*>(dout + base + col) : make_uint4(0, 0, 0, 0);
+      const int c = tid + 256 * it;
+      const int row = c / CPR, col = (c % CPR) * 8;
+      const int tok = t0 + row / G;
+      const int head = g * G + row % G;
+      const bool ok = tok < qhi;
+      const size_t off = (static_cast<size_t>(tok) * hq + head) * D + col;
+      qr[it] = ok ? *reinterpret_cast<const uint4*>(q + off) : make_uint4(0, 0, 0, 0);
+      dr[it] = ok ? *reinterpret_cast<const uint4*>(dout + off) : make_uint4(0, 0, 0, 0);
     }
     if (tid < 32) {
+      const int tok = t0 + tid / G;
+      const int head = g * G + tid % G;
+      const bool ok = tok < qhi;
       const size_t li = static_cast<size_t>(head) * nq + tok;
       lreg = ok ? lse[li] * kLog2e : kNegInf;
       dlreg = ok ? delta[li] : 0.f;
@@ -332,19 +337,12 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
     }
   };
   auto store_tile = [&](int b) {
-    const int row = tid & 31;
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
-      const int col = ((tid >> 5) + 8 * it) * 8;
-      *reinterpret_cast<uint4*>(&Qs[b][perm_row(row) * RROW + col]) = qr[it];
-      *reinterpret_cast<uint4*>(&Ds[b][perm_row(row) * RROW + col]) = dr[it];
-      const uint32_t wq[4] = {qr[it].x, qr[it].y, qr[it].z, qr[it].w};
-      const uint32_t wd[4] = {dr[it].x, dr[it].y, dr[it].z, dr[it].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        Qt[b][(col + e) * TROW + row] = static_cast<uint16_t>(wq[e >> 1] >> (16 * (e & 1)));
-        Dt[b][(col + e) * TROW + row] = static_cast<uint16_t>(wd[e >> 1] >> (16 * (e & 1)));
-      }
+      const int c = tid + 256 * it;
+      const int row = c / CPR, col = (c % CPR) * 8;
+      *reinterpret_cast<uint4*>(&Qs[b][toff<D>(row, col)]) = qr[it];
+      *reinterpret_cast<uint4*>(&Ds[b][toff<D>(row, col)]) = dr[it];
     }
     if (tid < 32) {
       lse_s[b][tid] = lreg;
@@ -365,7 +363,7 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
     const int t0 = qlo + t * TPT;
     if (t + 1 < ntiles) load_tile(t0 + TPT);
 
-    // tile rows 0..31 are sorted by (seq, pos); row 31 may be padding
+    // tile rows 0..31 are sorted by (seq, pos); trailing rows may be padding
     const int rl = min(qhi - t0, TPT) * G - 1;     // last valid row
     const int rf_seq = rseq_s[b][0], rf_pos = rpos_s[b][0];
     const int rl_seq = rseq_s[b][rl], rl_pos = rpos_s[b][rl];
@@ -375,24 +373,22 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
                            wf_seq == wl_seq && rf_pos >= wl_pos;
 
     if (wave_any) {
+      // S = Q K^T, dP = dO V^T: lane (n = key, hi) register r holds row acc_row(r, hi)
       f32x16 sacc = zero16(), dpacc = zero16();
-      const uint16_t* qp = &Qs[b][n * RROW + 8 * hi];
-      const uint16_t* dp = &Ds[b][n * RROW + 8 * hi];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        sacc = mfma32(lds_read8(qp + 16 * ks), kreg[ks], sacc);
-        dpacc = mfma32(lds_read8(dp + 16 * ks), vreg[ks], dpacc);
+        sacc = mfma32(row_operand<D>(Qs[b], lo_off, 0, ks), row_operand<D>(Kw, lo_off, wave * 32, ks), sacc);
+        dpacc = mfma32(row_operand<D>(Ds[b], lo_off, 0, ks), row_operand<D>(Vw, lo_off, wave * 32, ks), dpacc);
       }
-      // lane (n = key, hi) holds rows 16*hi + r
       float p[16], ds[16];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int rb = 16 * hi + 4 * r4;
+        const int rb = 8 * r4 + 4 * hi;
         const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[b][rb]);
         const float4 d4 = *reinterpret_cast<const float4*>(&dl_s[b][rb]);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
         const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-        int sv[4] = {0, 0, 0, 0}, pv[4] = {0, 0, 0, 0};
+        int sv[4] = {kseq, kseq, kseq, kseq}, pv[4] = {kpos, kpos, kpos, kpos};
         if (!wave_full) {
           const int4 ss = *reinterpret_cast<const int4*>(&rseq_s[b][rb]);
           const int4 pp = *reinterpret_cast<const int4*>(&rpos_s[b][rb]);
@@ -402,8 +398,7 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
-          const bool vis = key_valid && lv[e] != kNegInf &&
-                           (wave_full || (sv[e] == kseq && pv[e] >= kpos));
+          const bool vis = key_valid & (lv[e] != kNegInf) & (sv[e] == kseq) & (pv[e] >= kpos);
           const float pr = vis ? exp2_fast(sacc[r] * scale_log2 - lv[e]) : 0.f;
           p[r] = pr;
           ds[r] = pr * (dpacc[r] - dv4[e]);
@@ -411,8 +406,8 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
       }
       // dV^T += dO^T P, dK^T += Q^T dS  (k = 32 rows, 2 steps of 16).
       // P and dS enter the MFMA as bf16.  Where some P of the block reaches
-      // kSplitP, they enter as hi + lo bf16 pairs (lo = x - hi, a second MFMA
-      // on the same A operand): rows that give a key a large weight would
+      // kSplitP they enter as hi + lo bf16 pairs (lo = x - hi, a second MFMA on
+      // the same A operand): rows that give a key a large weight would
       // otherwise carry bf16's 2^-9 relative rounding into the key's gradient
       // with a large coefficient.  Below the threshold the dropped lo terms
       // are at most kSplitP * 2^-9 each.
@@ -422,24 +417,21 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
       const bool split = __any(big);
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        float ph[8], dh[8];
-        bf16x8 pb, db;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pb[j] = static_cast<__bf16>(p[8 * s2 + j]);
-          db[j] = static_cast<__bf16>(ds[8 * s2 + j]);
-          ph[j] = p[8 * s2 + j] - static_cast<float>(pb[j]);
-          dh[j] = ds[8 * s2 + j] - static_cast<float>(db[j]);
-        }
-        const uint16_t* dtp = &Dt[b][n * TROW + 16 * hi + 8 * s2];
-        const uint16_t* qtp = &Qt[b][n * TROW + 16 * hi + 8 * s2];
+        const bf16x8 pb = pack8(&p[8 * s2]);
+        const bf16x8 db = pack8(&ds[8 * s2]);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const bf16x8 at = lds_read8(dtp + mb * 32 * TROW);
-          const bf16x8 aq = lds_read8(qtp + mb * 32 * TROW);
+          const bf16x8 at = tr_operand<D>(Ds[b], lo_off, 16 * s2, mb);
+          const bf16x8 aq = tr_operand<D>(Qs[b], lo_off, 16 * s2, mb);
           dvacc[mb] = mfma32(at, pb, dvacc[mb]);
           dkacc[mb] = mfma32(aq, db, dkacc[mb]);
           if (split) {
+            float ph[8], dh[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              ph[j] = p[8 * s2 + j] - static_cast<float>(pb[j]);
+              dh[j] = ds[8 * s2 + j] - static_cast<float>(db[j]);
+            }
             dvacc[mb] = mfma32(at, pack8(ph), dvacc[mb]);
             dkacc[mb] = mfma32(aq, pack8(dh), dkacc[mb]);
           }

@@ -2,14 +2,25 @@
 //
 // MFMA used: v_mfma_f32_32x32x16_bf16 (A 32x16, B 16x32, C/D 32x32 fp32).
 // Lane l (n = l % 32, hi = l / 32) supplies row n of A and column n of B,
-// each as 8 consecutive k-elements of the half hi; accumulator register r of
-// lane l holds D[8*(r/4) + 4*hi + (r%4)][n].
+// each as 8 k-elements; accumulator register r of lane l holds
+// D[8*(r/4) + 4*hi + (r%4)][n].
 //
-// Row permutation rho: if A-operand lane n carries logical row rho(n), the
-// accumulator registers r = 0..15 of lane (n, hi) hold logical rows
-// 16*hi + r, i.e. each half-wave owns 16 consecutive rows.  Tiles are stored
-// in LDS with logical row t at LDS row rho_inv(t), so lane n always reads LDS
-// row n (consecutive rows, conflict-free with the row padding below).
+// Operand conventions used by every kernel here:
+//   * "row operand": a lane reads 16 contiguous bytes of one tile row
+//     (row n, k-elements 16*ks + 8*hi + 0..7) with ds_read_b128.
+//   * "transposed operand": the MFMA rows are tile COLUMNS col0 + n and the
+//     k-elements are tile rows kbase + 8*(j/4) + 4*hi + (j%4), j = 0..7.  Two
+//     ds_read_b64_tr_b16 produce it from a row-major tile: inside each 16-lane
+//     group, lanes pointing 4-per-row at 4 consecutive rows (16 columns) get
+//     that 4x16 block transposed, one column per lane.
+//   * "accumulator operand": registers r = 8*s + j (j = 0..7) of a 32x32
+//     accumulator, rounded to bf16, are the B operand of k-step s.  Their
+//     k-elements are accumulator rows 16*s + 8*(j/4) + 4*hi + (j%4), the same
+//     order as a transposed operand with kbase = 16*s.
+//
+// LDS tiles are row-major bf16 with the 16-byte chunks of each row XOR-swizzled
+// by the row index, so that both access patterns (16 consecutive rows at one
+// chunk, and 4 consecutive rows x 4 chunks) touch distinct banks.
 #pragma once
 
 #include "device_common.hpp"
@@ -17,24 +28,26 @@
 namespace bac {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-
-// rho(m) = 16*((m>>2)&1) + 4*(m>>3) + (m&3); rho_inv(t) = 8*((t>>2)&3) + 4*(t>>4) + (t&3).
-__host__ __device__ constexpr int rho(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
-__host__ __device__ constexpr int rho_inv(int t) { return 8 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3); }
-
-// Position of logical row t inside a tile made of 32-row blocks.
-__device__ __forceinline__ int perm_row(int t) { return (t & ~31) | rho_inv(t & 31); }
 
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
   for (int i = 0; i < 16; ++i) z[i] = 0.f;
   return z;
+}
+
+__device__ __forceinline__ bf16x8 zero8() {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = static_cast<__bf16>(0.f);
+  return r;
 }
 
 __device__ __forceinline__ bf16x8 pack8(const float* p) {
@@ -44,16 +57,70 @@ __device__ __forceinline__ bf16x8 pack8(const float* p) {
   return r;
 }
 
-__device__ __forceinline__ bf16x8 lds_read8(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
+// Swizzled position of 16-byte chunk c of row r in a tile with D columns.
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (D == 128) return c ^ ((4 * (r & 3)) | ((r >> 2) & 3));
+  else return c ^ ((4 * ((r >> 1) & 1)) | ((r >> 2) & 3));
 }
 
-__device__ __forceinline__ bf16x8 zero8() {
-  bf16x8 r;
+// Element offset of (row, col) in a swizzled tile; col % 4 == 0 keeps 8-byte alignment.
+template <int D>
+__device__ __forceinline__ int toff(int r, int col) {
+  return r * D + 8 * swz<D>(r, col >> 3) + (col & 7);
+}
+
+// Per-lane operand addressing.  The swizzle depends only on row & 15, so for
+// tile rows that differ by multiples of 16 a lane's offsets differ by the
+// plain row stride: each lane precomputes its offsets once, and the kernels
+// add compile-time row offsets (which fold into the LDS instruction's
+// immediate offset).
+template <int D>
+struct LaneOffsets {
+  static constexpr int KS = D / 16;
+  static constexpr int MB = D / 32;
+  int row[KS];       // row operand: tile row n, columns 16*ks + 8*hi .. +7
+  int tr[MB][2];     // transposed operand: column block mb, first / second read
+  __device__ __forceinline__ explicit LaneOffsets(int lane) {
+    const int n = lane & 31, hi = lane >> 5;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = static_cast<__bf16>(0.f);
+    for (int ks = 0; ks < KS; ++ks) row[ks] = toff<D>(n, 16 * ks + 8 * hi);
+    const int g = lane >> 4, i = lane & 15;
+    const int r0 = 4 * (g >> 1) + (i >> 2);
+    const int c0 = 16 * (g & 1) + 4 * (i & 3);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      tr[mb][0] = toff<D>(r0, 32 * mb + c0);
+      tr[mb][1] = toff<D>(r0 + 8, 32 * mb + c0);
+    }
+  }
+};
+
+// Row operand: tile row (row16 + n) where row16 % 16 == 0, k-step ks.
+template <int D>
+__device__ __forceinline__ bf16x8 row_operand(const uint16_t* tile, const LaneOffsets<D>& lo,
+                                              int row16, int ks) {
+  return *reinterpret_cast<const bf16x8*>(tile + row16 * D + lo.row[ks]);
+}
+
+// Transposed operand: MFMA rows = tile columns 32*mb + n, k-elements = tile
+// rows kbase + 8*(j/4) + 4*hi + (j%4), kbase % 16 == 0.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, const LaneOffsets<D>& lo,
+                                             int kbase, int mb) {
+  // generic -> LDS address space (the tile lives in __shared__ memory)
+  lds_bf16x4* p0 = (lds_bf16x4*)(tile + kbase * D + lo.tr[mb][0]);
+  lds_bf16x4* p1 = (lds_bf16x4*)(tile + kbase * D + lo.tr[mb][1]);
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p0);
+  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p1);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
   return r;
 }
+
+// Accumulator row of register r for lane half hi.
+__device__ __forceinline__ int acc_row(int r, int hi) { return 8 * (r >> 2) + 4 * hi + (r & 3); }
 
 // XCD-aware block order: hardware dispatches block b to XCD b % 8.  Give
 // every XCD a contiguous range of logical blocks so that blocks sharing K/V

@@ -11,15 +11,18 @@
 //     of one kv-head group: 256 (token, q-head) rows that all read the same
 //     K/V tiles.  Wave w owns 32 rows: tokens tok0 + w*32/G + n/G, heads
 //     g*G + n%G for n = 0..31 (the GQA heads of a token are adjacent rows).
-//   * Keys stream through LDS in tiles of 64, double buffered, one barrier per
-//     tile.  The key range of a workgroup is [first key of its first row's
-//     sequence, last key visible to its last row], found by binary search on
-//     the (seq, pos)-sorted shard.
+//   * Keys stream through LDS in row-major tiles of 64, double buffered, one
+//     barrier per tile.  The key range of a workgroup is [first key of its
+//     first row's sequence, last key visible to its last row], found by binary
+//     search on the (seq, pos)-sorted shard.
 //   * Scores are computed transposed, S^T = K Q^T (keys x rows), so each lane
 //     holds 32 scores of ONE query row: the row max is in-lane plus one
 //     exchange with lane n+32, and the row sums stay per lane until the end.
-//   * O^T += V^T P^T with P^T taken straight from the score registers
-//     (rounded to bf16) and V^T read from a transposed LDS copy of the tile.
+//   * O^T += V^T P^T: P^T comes straight from the score registers (bf16),
+//     V^T from transposing LDS reads of the row-major V tile.
+//   * Lazy rescale: the running max only moves when a tile's max exceeds it by
+//     more than 8 (log2 units), so P stays below 2^8 and most tiles skip the
+//     rescale of O.  Normalisation by the row sum makes this exact.
 //   * Tiles wholly visible to a wave skip the mask; tiles wholly beyond a
 //     wave's rows skip the compute.
 //   * Blocks are ordered heavy-first (later tokens see more keys) and remapped
@@ -33,10 +36,9 @@
 namespace bac {
 
 namespace fwd {
-constexpr int BN = 64;        // keys per tile
-constexpr int NW = 8;         // waves per workgroup
-constexpr int KPAD = 8;       // bf16 pad per K row in LDS
-constexpr int VPAD = 8;       // bf16 pad per V^T row in LDS
+constexpr int BN = 64;          // keys per tile
+constexpr int NW = 8;           // waves per workgroup
+constexpr float kRescale = 8.f; // lazy-rescale threshold (log2 units)
 }  // namespace fwd
 
 template <int D, int G>
@@ -51,13 +53,11 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
   constexpr int TPB = NW * TPW;         // tokens per workgroup
   constexpr int KS = D / 16;            // k-steps of QK^T
   constexpr int MB = D / 32;            // 32-row blocks of O^T
-  constexpr int KROW = D + KPAD;
-  constexpr int VROW = BN + VPAD;
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int LOADS = BN * CPR / 512; // 16-byte chunks per thread per tile
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * D];
   __shared__ __attribute__((aligned(16))) int kseq_s[2][BN];
   __shared__ __attribute__((aligned(16))) int kpos_s[2][BN];
 
@@ -69,6 +69,7 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, hi = lane >> 5;
+  const LaneOffsets<D> lo_off(lane);
 
   // ---- this lane's query row -------------------------------------------
   const int wtok0 = tok0 + wave * TPW;
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
   f32x16 oacc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) oacc[mb] = zero16();
-  float m_run = kNegInf;   // running max (log2 units), same in lanes n and n+32
+  float m_run = kNegInf;   // reference max (log2 units), same in lanes n and n+32
   float l_run = 0.f;       // this lane's part of the running sum
 
   // ---- tile staging: global -> registers -> LDS ---------------------------
@@ -136,11 +137,8 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
     for (int it = 0; it < LOADS; ++it) {
       const int c = tid + 512 * it;
       const int key = c / CPR, col = (c % CPR) * 8;
-      *reinterpret_cast<uint4*>(&Ks[b][perm_row(key) * KROW + col]) = kreg[it];
-      const uint32_t w[4] = {vreg[it].x, vreg[it].y, vreg[it].z, vreg[it].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        Vt[b][(col + e) * VROW + key] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+      *reinterpret_cast<uint4*>(&Ks[b][toff<D>(key, col)]) = kreg[it];
+      *reinterpret_cast<uint4*>(&Vs[b][toff<D>(key, col)]) = vreg[it];
     }
     if (tid < BN) {
       kseq_s[b][tid] = sreg;
@@ -169,16 +167,16 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
                            kf_seq == wf_seq && wf_seq == wl_seq && kl_pos <= wf_pos;
 
     if (wave_any) {
-      // S^T = K Q^T: two 32-key blocks
+      // S^T = K Q^T over two 32-key blocks: lane (n, hi) register r of block kb
+      // holds key kb*32 + acc_row(r, hi) of query row n.
       f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         sacc[kb] = zero16();
-        const uint16_t* kp = &Ks[b][(kb * 32 + n) * KROW + 8 * hi];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sacc[kb] = mfma32(lds_read8(kp + 16 * ks), qreg[ks], sacc[kb]);
+        for (int ks = 0; ks < KS; ++ks)
+          sacc[kb] = mfma32(row_operand<D>(Ks[b], lo_off, kb * 32, ks), qreg[ks], sacc[kb]);
       }
-      // lane (n, hi) now holds keys kb*32 + 16*hi + r, r = 0..15, of row n
       float x[2][16];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -186,54 +184,55 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
         for (int r = 0; r < 16; ++r) x[kb][r] = sacc[kb][r] * scale_log2;
       if (!wave_full) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int tb0 = kb * 32 + 16 * hi;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            const int4 ss = *reinterpret_cast<const int4*>(&kseq_s[b][tb0 + 4 * r4]);
-            const int4 pp = *reinterpret_cast<const int4*>(&kpos_s[b][tb0 + 4 * r4]);
+            const int t0 = kb * 32 + 8 * r4 + 4 * hi;
+            const int4 ss = *reinterpret_cast<const int4*>(&kseq_s[b][t0]);
+            const int4 pp = *reinterpret_cast<const int4*>(&kpos_s[b][t0]);
             const int sv[4] = {ss.x, ss.y, ss.z, ss.w};
             const int pv[4] = {pp.x, pp.y, pp.z, pp.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const bool vis = row_valid && sv[e] == my_seq && pv[e] <= my_pos;
-              if (!vis) x[kb][4 * r4 + e] = kNegInf;
+              const bool vis = row_valid & (sv[e] == my_seq) & (pv[e] <= my_pos);
+              x[kb][4 * r4 + e] = vis ? x[kb][4 * r4 + e] : kNegInf;
             }
           }
-        }
       }
       float mt = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, x[kb][r]);
+        for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(x[kb][r], x[kb][r + 1]));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      float ls = 0.f;
+      // lazy rescale: move the reference only when the tile max clears it by kRescale
+      if (__any(mt > m_run + kRescale)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = (m_run == kNegInf) ? 0.f : exp2_fast(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == kNegInf) ? 0.f : m_run;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           x[kb][r] = exp2_fast(x[kb][r] - m_use);
-          ls += x[kb][r];
+          l_run += x[kb][r];
         }
-      l_run = l_run * alpha + ls;
-      m_run = m_new;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
       // O^T += V^T P^T, four k-steps of 16 keys
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const bf16x8 pb = pack8(&x[kb][8 * s2]);
-          const uint16_t* vp = &Vt[b][n * VROW + kb * 32 + 16 * hi + 8 * s2];
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) oacc[mb] = mfma32(lds_read8(vp + mb * 32 * VROW), pb, oacc[mb]);
+          for (int mb = 0; mb < MB; ++mb)
+            oacc[mb] = mfma32(tr_operand<D>(Vs[b], lo_off, kb * 32 + 16 * s2, mb), pb, oacc[mb]);
         }
     }
 
