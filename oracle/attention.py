@@ -57,11 +57,12 @@ def lse_merge(o_a, lse_a, o_b, lse_b):
     return o, lse
 
 
-def partial(prob: Problem, rows, keys):
+def partial(prob: Problem, rows, keys, heads=None):
     """Softmax attention of ``rows`` over the subset ``keys`` under the mask.
 
     Returns O [R, Hq, d] and lse [R, Hq]; a row that sees none of the keys gets
-    O = 0 and lse = -inf.
+    O = 0 and lse = -inf.  ``heads`` restricts the evaluation to those q-heads
+    (the others are left at O = 0, lse = -inf).
     """
     rows = np.asarray(rows, dtype=np.int64)
     keys = np.asarray(keys, dtype=np.int64)
@@ -72,7 +73,7 @@ def partial(prob: Problem, rows, keys):
         return O, lse
     mask = prob.visibility(rows, keys)
     Q, K, V = prob.qrows(rows), prob.krows(keys), prob.vrows(keys)
-    for h in range(prob.hq):
+    for h in (range(prob.hq) if heads is None else heads):
         g = prob.group[h]
         S = prob.scale * (Q[:, h, :] @ K[:, g, :].T)
         S = np.where(mask, S, _NEG_INF)
@@ -93,11 +94,12 @@ def delta(O, dO):
     return np.einsum("rhd,rhd->rh", np.asarray(dO, np.float64), np.asarray(O, np.float64))
 
 
-def grads(prob: Problem, rows, keys, lse, dO, dlt):
+def grads(prob: Problem, rows, keys, lse, dO, dlt, heads=None):
     """Gradient contributions of the (rows x keys) block, recomputed from the
     merged lse of the rows.
 
     Returns dQ [R, Hq, d] (this block's share) and dK, dV [len(keys), Hkv, d].
+    ``heads`` restricts the sums to those q-heads.
     """
     rows = np.asarray(rows, dtype=np.int64)
     keys = np.asarray(keys, dtype=np.int64)
@@ -111,7 +113,7 @@ def grads(prob: Problem, rows, keys, lse, dO, dlt):
     Q, K, V = prob.qrows(rows), prob.krows(keys), prob.vrows(keys)
     dO = np.asarray(dO, dtype=np.float64)
     lse = np.asarray(lse, dtype=np.float64)
-    for h in range(prob.hq):
+    for h in (range(prob.hq) if heads is None else heads):
         g = prob.group[h]
         S = prob.scale * (Q[:, h, :] @ K[:, g, :].T)
         ref = np.where(np.isfinite(lse[:, h]), lse[:, h], 0.0)
@@ -192,19 +194,19 @@ def forward_decomposed(prob: Problem):
 # Sampled evaluation for workloads too large for the full oracle.
 # ---------------------------------------------------------------------------
 
-def forward_rows(prob: Problem, rows):
+def forward_rows(prob: Problem, rows, heads=None):
     """O, lse of the given rows only, each over its full visible key set."""
     rows = np.asarray(rows, dtype=np.int64)
-    return partial(prob, rows, prob.visible_keys(rows))
+    return partial(prob, rows, prob.visible_keys(rows), heads)
 
 
-def backward_rows(prob: Problem, rows, dO_rows):
+def backward_rows(prob: Problem, rows, dO_rows, heads=None):
     """dQ of the given rows (their O, lse and Delta computed here)."""
     rows = np.asarray(rows, dtype=np.int64)
     keys = prob.visible_keys(rows)
-    O, lse = partial(prob, rows, keys)
+    O, lse = partial(prob, rows, keys, heads)
     dlt = delta(O, dO_rows)
-    dq, _, _ = grads(prob, rows, keys, lse, dO_rows, dlt)
+    dq, _, _ = grads(prob, rows, keys, lse, dO_rows, dlt, heads)
     return dq, O, lse
 
 
@@ -237,14 +239,14 @@ def key_grads(prob: Problem, keys, dO_source, heads=None, row_chunk=64):
     for i in range(0, rows.shape[0], row_chunk):
         r = rows[i:i + row_chunk]
         full = prob.visible_keys(r)
-        O, lse = partial(prob, r, full)
+        O, lse = partial(prob, r, full, heads)
         dO = np.asarray(dO_source[r], dtype=np.float64)
         if heads is not None:
             keep = np.zeros(prob.hq, bool)
             keep[list(heads)] = True
             dO = np.where(keep[None, :, None], dO, 0.0)
         dlt = delta(O, dO)
-        _, dk, dv = grads(prob, r, keys, lse, dO, dlt)
+        _, dk, dv = grads(prob, r, keys, lse, dO, dlt, heads)
         dK += dk
         dV += dv
     return dK, dV
