@@ -187,20 +187,25 @@ def build_step(torch, api, ring, w, st, t, dev, timer):
     return step, work, ri, pl, bufs
 
 
-def traffic_for(kernel, launches_per_step, flops_per_launch):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; None otherwise."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/<kernel>_<workload>.md: FETCH_SIZE and WRITE_SIZE passes scaled by
+    a plain-copy calibration), only while the kernel source is the profiled one."""
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAMES[kernel]}_{workload}.md")
     if not os.path.exists(path):
         return None
-    try:
-        with open(path) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
-        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                rec[k.strip()] = v.strip()
     if rec.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, st, t, n_anchor, log_fn):
@@ -322,7 +327,7 @@ def main():
     flops_per_launch = timer.work[dom] / n_launch
     avg_s = timer.total[dom] / n_launch
     achieved = flops_per_launch / avg_s / 1e12
-    traffic = traffic_for(dom, n_launch // max(args.steps, 1), flops_per_launch)
+    traffic = traffic_for(dom, w.name)
     roofline = dict(bound="mfma", kernel=KERNEL_NAMES[dom], achieved=round(achieved, 1),
                     peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4),
                     traffic=traffic, avg_launch_ms=round(avg_s * 1e3, 3),
