@@ -19,6 +19,7 @@
 // is race-free within a launch and ordered across launches on one stream.
 
 #include <climits>
+#include <type_traits>
 
 #include "launch.hpp"
 #include "mfma_common.hpp"
@@ -225,12 +226,27 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 // dK / dV: key-outer.  K and V of the workgroup's 128 keys stay in LDS; the
 // query rows that can see them stream through in tiles of 32 rows.
+//
+// Query tiles are visited from the END of the visible range backwards: every
+// key block of a sequence sees the same trailing rows, so the workgroups that
+// an XCD runs together read the same tiles at nearly the same time and share
+// them through L2 (front-to-back, their start rows differ and they do not).
+// Tiles arrive by direct global->LDS loads through a ring of NSTAGE buffers,
+// issued three tiles ahead with one barrier per tile.  Each stage is its own
+// __shared__ array so the compiler can tell the in-flight loads of one stage
+// from the reads of another and does not drain the whole pipeline.
 // ---------------------------------------------------------------------------
 namespace bwdkv {
 constexpr int NW = 4;          // waves per workgroup, 32 keys each
 constexpr int KB = NW * 32;    // keys per workgroup
+constexpr int NSTAGE = 4;      // tile buffers in the load ring
 constexpr float kSplitP = 1.f / 256.f;
+// s_waitcnt immediate that waits until at most n vector-memory ops are
+// outstanding (gfx9 encoding; expcnt / lgkmcnt left at their maxima).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0xF70; }
 }  // namespace bwdkv
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <int D, int G>
 __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
@@ -245,17 +261,16 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
   constexpr int KS = D / 16;
   constexpr int MB = D / 32;
   constexpr int CPR = D / 8;
-  constexpr int LOADS = 32 * CPR / 256;     // 16-byte chunks per thread per tile (per tensor)
-  constexpr int KLOADS = KB * CPR / 256;    // chunks per thread for the K / V block
+  constexpr int KLOADS = KB * CPR / 256;    // 16-byte chunks per thread for the K / V block
+  constexpr int QROUNDS = 32 * CPR / 256;   // 16-byte DMA rounds per thread per tensor per tile
+  constexpr int PER_TILE = 2 * QROUNDS + 1; // DMA ops per thread per tile (Q, dO, one meta array)
 
   __shared__ __attribute__((aligned(16))) uint16_t Kw[KB * D];     // keys x d, swizzled
   __shared__ __attribute__((aligned(16))) uint16_t Vw[KB * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][32 * D];  // rows x d, swizzled
-  __shared__ __attribute__((aligned(16))) uint16_t Ds[2][32 * D];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][32];
-  __shared__ __attribute__((aligned(16))) float dl_s[2][32];
-  __shared__ __attribute__((aligned(16))) int rseq_s[2][32];
-  __shared__ __attribute__((aligned(16))) int rpos_s[2][32];
+  // tile ring: rows x d (swizzled) for Q and dO; meta = lse | delta | seq | pos, 64 words each
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[32 * D], Q1[32 * D], Q2[32 * D], Q3[32 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t O0[32 * D], O1[32 * D], O2[32 * D], O3[32 * D];
+  __shared__ __attribute__((aligned(16))) uint32_t M0s[256], M1s[256], M2s[256], M3s[256];
 
   const float scale_log2 = scale * kLog2e;
   const int nblk = (nk + KB - 1) / KB;
@@ -295,8 +310,10 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
     *reinterpret_cast<uint4*>(&Kw[toff<D>(kr, col)]) = kk;
     *reinterpret_cast<uint4*>(&Vw[toff<D>(kr, col)]) = vv;
   }
+  __syncthreads();
 
-  // query tokens that can see any key of the block
+  // query tokens that can see any key of the block; tiles are taken from the
+  // end: tile i covers tokens [qhi - (i+1)*TPT, qhi - i*TPT) clipped at qlo
   const int klast = min(nk, key0 + KB) - 1;
   const int qlo = lower_bound_sp(q_seq, q_pos, nq, k_seq[key0], k_pos[key0]);
   const int qhi = upper_bound_sp(q_seq, q_pos, nq, k_seq[klast], INT_MAX);
@@ -309,138 +326,168 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
     dvacc[mb] = zero16();
   }
 
-  // staging: chunk c -> (row = c / CPR, col); a row is (token t0 + row / G, head g*G + row % G)
-  uint4 qr[LOADS], dr[LOADS];
-  float lreg = 0.f, dlreg = 0.f;
-  int sreg = 0, preg = 0;
-  auto load_tile = [&](int t0) {
+  auto qbuf = [&](auto S) -> uint16_t* {
+    if constexpr (S == 0) return Q0; else if constexpr (S == 1) return Q1;
+    else if constexpr (S == 2) return Q2; else return Q3;
+  };
+  auto obuf = [&](auto S) -> uint16_t* {
+    if constexpr (S == 0) return O0; else if constexpr (S == 1) return O1;
+    else if constexpr (S == 2) return O2; else return O3;
+  };
+  auto mbuf = [&](auto S) -> uint32_t* {
+    if constexpr (S == 0) return M0s; else if constexpr (S == 1) return M1s;
+    else if constexpr (S == 2) return M2s; else return M3s;
+  };
+
+  // First token of tile i (tiles taken from the end of [qlo, qhi)).
+  auto tile_t0 = [&](int i) { return max(qlo, qhi - (i + 1) * TPT); };
+
+  // Issue the loads of tile i into stage S.  Lane l of round `it` of wave w
+  // fills 16-byte slot (it*NW + w)*64 + l of the tile, i.e. physical chunk p of
+  // row r; it fetches logical chunk swz(r, p) (the swizzle is an involution).
+  // Rows past the tile's end re-read its last row; they are masked by index.
+  auto issue = [&](auto S, int i) {
+    uint16_t* qd = qbuf(S);
+    uint16_t* od = obuf(S);
+    uint32_t* md = mbuf(S);
+    const int t0 = tile_t0(i);
+    const int t1 = qhi - i * TPT;              // one past the tile's last token
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int c = tid + 256 * it;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      const int tok = t0 + row / G;
-      const int head = g * G + row % G;
-      const bool ok = tok < qhi;
-      const size_t off = (static_cast<size_t>(tok) * hq + head) * D + col;
-      qr[it] = ok ? *reinterpret_cast<const uint4*>(q + off) : make_uint4(0, 0, 0, 0);
-      dr[it] = ok ? *reinterpret_cast<const uint4*>(dout + off) : make_uint4(0, 0, 0, 0);
+    for (int it = 0; it < QROUNDS; ++it) {
+      const int slot = (it * NW + wave) * 64 + lane;
+      const int r = slot / CPR, p = slot % CPR;
+      const int c = swz<D>(r, p);
+      const int tok = min(t0 + r / G, t1 - 1);
+      const int head = g * G + r % G;
+      const size_t off = (static_cast<size_t>(tok) * hq + head) * D + 8 * c;
+      const int base = (it * NW + wave) * 64 * 8;
+      __builtin_amdgcn_global_load_lds(q + off, (lds_void*)(qd + base), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(dout + off, (lds_void*)(od + base), 16, 0, 0);
     }
-    if (tid < 32) {
-      const int tok = t0 + tid / G;
-      const int head = g * G + tid % G;
-      const bool ok = tok < qhi;
+    {
+      const int r = lane & 31;
+      const int tok = min(t0 + r / G, t1 - 1);
+      const int head = g * G + r % G;
       const size_t li = static_cast<size_t>(head) * nq + tok;
-      lreg = ok ? lse[li] * kLog2e : kNegInf;
-      dlreg = ok ? delta[li] : 0.f;
-      sreg = ok ? q_seq[tok] : INT_MAX;
-      preg = ok ? q_pos[tok] : INT_MIN;
-    }
-  };
-  auto store_tile = [&](int b) {
-#pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int c = tid + 256 * it;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      *reinterpret_cast<uint4*>(&Qs[b][toff<D>(row, col)]) = qr[it];
-      *reinterpret_cast<uint4*>(&Ds[b][toff<D>(row, col)]) = dr[it];
-    }
-    if (tid < 32) {
-      lse_s[b][tid] = lreg;
-      dl_s[b][tid] = dlreg;
-      rseq_s[b][tid] = sreg;
-      rpos_s[b][tid] = preg;
+      const void* src = wave == 0 ? static_cast<const void*>(lse + li)
+                      : wave == 1 ? static_cast<const void*>(delta + li)
+                      : wave == 2 ? static_cast<const void*>(q_seq + tok)
+                                  : static_cast<const void*>(q_pos + tok);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(md + wave * 64), 4, 0, 0);
     }
   };
 
-  if (ntiles > 0) {
-    load_tile(qlo);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int b = t & 1;
-    const int t0 = qlo + t * TPT;
-    if (t + 1 < ntiles) load_tile(t0 + TPT);
-
-    // tile rows 0..31 are sorted by (seq, pos); trailing rows may be padding
-    const int rl = min(qhi - t0, TPT) * G - 1;     // last valid row
-    const int rf_seq = rseq_s[b][0], rf_pos = rpos_s[b][0];
-    const int rl_seq = rseq_s[b][rl], rl_pos = rpos_s[b][rl];
+  auto compute = [&](auto S, int i) {
+    const uint16_t* Qs = qbuf(S);
+    const uint16_t* Ds = obuf(S);
+    const uint32_t* M = mbuf(S);
+    const float* lse_s = reinterpret_cast<const float*>(M);
+    const float* dl_s = reinterpret_cast<const float*>(M + 64);
+    const int* rseq_s = reinterpret_cast<const int*>(M + 128);
+    const int* rpos_s = reinterpret_cast<const int*>(M + 192);
+    const int t0 = tile_t0(i);
+    const int nrows = (qhi - i * TPT - t0) * G;   // valid rows of this tile
+    const int rl = nrows - 1;
+    const int rf_seq = rseq_s[0], rf_pos = rpos_s[0];
+    const int rl_seq = rseq_s[rl], rl_pos = rpos_s[rl];
     const bool wave_any = wave_valid && !lex_less(rl_seq, rl_pos, wf_seq, wf_pos) &&
                           !lex_less(wl_seq, INT_MAX, rf_seq, rf_pos);
     const bool wave_full = wave_complete && rl == 31 && rf_seq == rl_seq && rf_seq == wf_seq &&
                            wf_seq == wl_seq && rf_pos >= wl_pos;
-
-    if (wave_any) {
-      // S = Q K^T, dP = dO V^T: lane (n = key, hi) register r holds row acc_row(r, hi)
-      f32x16 sacc = zero16(), dpacc = zero16();
+    if (!wave_any) return;
+    // S = Q K^T, dP = dO V^T: lane (n = key, hi) register r holds row acc_row(r, hi)
+    f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        sacc = mfma32(row_operand<D>(Qs[b], lo_off, 0, ks), row_operand<D>(Kw, lo_off, wave * 32, ks), sacc);
-        dpacc = mfma32(row_operand<D>(Ds[b], lo_off, 0, ks), row_operand<D>(Vw, lo_off, wave * 32, ks), dpacc);
+    for (int ks = 0; ks < KS; ++ks) {
+      sacc = mfma32(row_operand<D>(Qs, lo_off, 0, ks), row_operand<D>(Kw, lo_off, wave * 32, ks), sacc);
+      dpacc = mfma32(row_operand<D>(Ds, lo_off, 0, ks), row_operand<D>(Vw, lo_off, wave * 32, ks), dpacc);
+    }
+    float p[16], ds[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int rb = 8 * r4 + 4 * hi;
+      const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[rb]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&dl_s[rb]);
+      const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+      int sv[4] = {kseq, kseq, kseq, kseq}, pv[4] = {kpos, kpos, kpos, kpos};
+      if (!wave_full) {
+        const int4 ss = *reinterpret_cast<const int4*>(&rseq_s[rb]);
+        const int4 pp = *reinterpret_cast<const int4*>(&rpos_s[rb]);
+        sv[0] = ss.x; sv[1] = ss.y; sv[2] = ss.z; sv[3] = ss.w;
+        pv[0] = pp.x; pv[1] = pp.y; pv[2] = pp.z; pv[3] = pp.w;
       }
-      float p[16], ds[16];
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int rb = 8 * r4 + 4 * hi;
-        const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[b][rb]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&dl_s[b][rb]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-        int sv[4] = {kseq, kseq, kseq, kseq}, pv[4] = {kpos, kpos, kpos, kpos};
-        if (!wave_full) {
-          const int4 ss = *reinterpret_cast<const int4*>(&rseq_s[b][rb]);
-          const int4 pp = *reinterpret_cast<const int4*>(&rpos_s[b][rb]);
-          sv[0] = ss.x; sv[1] = ss.y; sv[2] = ss.z; sv[3] = ss.w;
-          pv[0] = pp.x; pv[1] = pp.y; pv[2] = pp.z; pv[3] = pp.w;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          const bool vis = key_valid & (lv[e] != kNegInf) & (sv[e] == kseq) & (pv[e] >= kpos);
-          const float pr = vis ? exp2_fast(sacc[r] * scale_log2 - lv[e]) : 0.f;
-          p[r] = pr;
-          ds[r] = pr * (dpacc[r] - dv4[e]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * r4 + e;
+        const bool vis = key_valid & (rb + e < nrows) & (lv[e] != kNegInf) & (sv[e] == kseq) &
+                         (pv[e] >= kpos);
+        const float pr = vis ? exp2_fast(sacc[r] * scale_log2 - lv[e]) : 0.f;
+        p[r] = pr;
+        ds[r] = pr * (dpacc[r] - dv4[e]);
       }
-      // dV^T += dO^T P, dK^T += Q^T dS  (k = 32 rows, 2 steps of 16).
-      // P and dS enter the MFMA as bf16.  Where some P of the block reaches
-      // kSplitP they enter as hi + lo bf16 pairs (lo = x - hi, a second MFMA on
-      // the same A operand): rows that give a key a large weight would
-      // otherwise carry bf16's 2^-9 relative rounding into the key's gradient
-      // with a large coefficient.  Below the threshold the dropped lo terms
-      // are at most kSplitP * 2^-9 each.
-      bool big = false;
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS  (k = 32 rows, 2 steps of 16).
+    // P and dS enter the MFMA as bf16.  Where some P of the block reaches
+    // kSplitP they enter as hi + lo bf16 pairs (lo = x - hi, a second MFMA on
+    // the same A operand): rows that give a key a large weight would otherwise
+    // carry bf16's 2^-9 relative rounding into the key's gradient with a large
+    // coefficient.  Below the threshold the dropped lo terms are at most
+    // kSplitP * 2^-9 each.
+    bool big = false;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) big |= p[r] >= kSplitP;
-      const bool split = __any(big);
+    for (int r = 0; r < 16; ++r) big |= p[r] >= kSplitP;
+    const bool split = __any(big);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 pb = pack8(&p[8 * s2]);
-        const bf16x8 db = pack8(&ds[8 * s2]);
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const bf16x8 pb = pack8(&p[8 * s2]);
+      const bf16x8 db = pack8(&ds[8 * s2]);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const bf16x8 at = tr_operand<D>(Ds[b], lo_off, 16 * s2, mb);
-          const bf16x8 aq = tr_operand<D>(Qs[b], lo_off, 16 * s2, mb);
-          dvacc[mb] = mfma32(at, pb, dvacc[mb]);
-          dkacc[mb] = mfma32(aq, db, dkacc[mb]);
-          if (split) {
-            float ph[8], dh[8];
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 at = tr_operand<D>(Ds, lo_off, 16 * s2, mb);
+        const bf16x8 aq = tr_operand<D>(Qs, lo_off, 16 * s2, mb);
+        dvacc[mb] = mfma32(at, pb, dvacc[mb]);
+        dkacc[mb] = mfma32(aq, db, dkacc[mb]);
+        if (split) {
+          float ph[8], dh[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              ph[j] = p[8 * s2 + j] - static_cast<float>(pb[j]);
-              dh[j] = ds[8 * s2 + j] - static_cast<float>(db[j]);
-            }
-            dvacc[mb] = mfma32(at, pack8(ph), dvacc[mb]);
-            dkacc[mb] = mfma32(aq, pack8(dh), dkacc[mb]);
+          for (int j = 0; j < 8; ++j) {
+            ph[j] = p[8 * s2 + j] - static_cast<float>(pb[j]);
+            dh[j] = ds[8 * s2 + j] - static_cast<float>(db[j]);
           }
+          dvacc[mb] = mfma32(at, pack8(ph), dvacc[mb]);
+          dkacc[mb] = mfma32(aq, pack8(dh), dkacc[mb]);
         }
       }
     }
+  };
 
-    if (t + 1 < ntiles) store_tile(b ^ 1);
-    __syncthreads();
+  // One tile: wait until its loads are done (the two later tiles' loads may
+  // still be in flight), barrier (all waves' loads visible; every wave is done
+  // with the stage about to be refilled), refill that stage three tiles
+  // ahead, compute.
+  auto step = [&](auto S, int i) {
+    const int ahead = min(2, ntiles - 1 - i);
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * PER_TILE));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_TILE));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    if (i + 3 < ntiles) issue(std::integral_constant<int, (S + 3) % NSTAGE>{}, i + 3);
+    compute(S, i);
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  if (ntiles > 0) issue(I0{}, 0);
+  if (ntiles > 1) issue(I1{}, 1);
+  if (ntiles > 2) issue(I2{}, 2);
+  for (int i = 0; i < ntiles; i += NSTAGE) {
+    step(I0{}, i);
+    if (i + 1 < ntiles) step(I1{}, i + 1);
+    if (i + 2 < ntiles) step(I2{}, i + 2);
+    if (i + 3 < ntiles) step(I3{}, i + 3);
   }
 
   if (!key_valid) return;
