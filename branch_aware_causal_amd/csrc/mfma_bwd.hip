@@ -174,22 +174,25 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
                          row_operand<D>(my_do, lo_off, 0, ks), dpacc);
         }
         float ds[16];
+        if (wave_full) {
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          int sv[4] = {my_seq, my_seq, my_seq, my_seq}, pv[4] = {0, 0, 0, 0};
-          if (!wave_full) {
+          for (int r = 0; r < 16; ++r)
+            ds[r] = exp2_fast(fmaf(sacc[r], scale_log2, -lse_use)) * (dpacc[r] - my_delta);
+        } else {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
             const int t0 = kb * 32 + 8 * r4 + 4 * hi;
             const int4 ss = *reinterpret_cast<const int4*>(&kseq_s[b][t0]);
             const int4 pp = *reinterpret_cast<const int4*>(&kpos_s[b][t0]);
-            sv[0] = ss.x; sv[1] = ss.y; sv[2] = ss.z; sv[3] = ss.w;
-            pv[0] = pp.x; pv[1] = pp.y; pv[2] = pp.z; pv[3] = pp.w;
-          }
+            const int sv[4] = {ss.x, ss.y, ss.z, ss.w};
+            const int pv[4] = {pp.x, pp.y, pp.z, pp.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * r4 + e;
-            const bool vis = row_live & (sv[e] == my_seq) & (pv[e] <= my_pos);
-            const float p = exp2_fast(sacc[r] * scale_log2 - lse_use);
-            ds[r] = vis ? p * (dpacc[r] - my_delta) : 0.f;
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * r4 + e;
+              const bool vis = row_live & (sv[e] == my_seq) & (pv[e] <= my_pos);
+              const float p = exp2_fast(fmaf(sacc[r], scale_log2, -lse_use));
+              ds[r] = vis ? p * (dpacc[r] - my_delta) : 0.f;
+            }
           }
         }
         // dQ^T += K^T dS^T over the 32 keys of this block (2 k-steps)
@@ -410,21 +413,28 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
       const float4 d4 = *reinterpret_cast<const float4*>(&dl_s[rb]);
       const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
       const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-      int sv[4] = {kseq, kseq, kseq, kseq}, pv[4] = {kpos, kpos, kpos, kpos};
-      if (!wave_full) {
+      if (wave_full) {
+        // every row valid and every key visible: no mask
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          p[r] = exp2_fast(fmaf(sacc[r], scale_log2, -lv[e]));
+          ds[r] = p[r] * (dpacc[r] - dv4[e]);
+        }
+      } else {
         const int4 ss = *reinterpret_cast<const int4*>(&rseq_s[rb]);
         const int4 pp = *reinterpret_cast<const int4*>(&rpos_s[rb]);
-        sv[0] = ss.x; sv[1] = ss.y; sv[2] = ss.z; sv[3] = ss.w;
-        pv[0] = pp.x; pv[1] = pp.y; pv[2] = pp.z; pv[3] = pp.w;
-      }
+        const int sv[4] = {ss.x, ss.y, ss.z, ss.w};
+        const int pv[4] = {pp.x, pp.y, pp.z, pp.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * r4 + e;
-        const bool vis = key_valid & (rb + e < nrows) & (lv[e] != kNegInf) & (sv[e] == kseq) &
-                         (pv[e] >= kpos);
-        const float pr = vis ? exp2_fast(sacc[r] * scale_log2 - lv[e]) : 0.f;
-        p[r] = pr;
-        ds[r] = pr * (dpacc[r] - dv4[e]);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          const bool vis = key_valid & (rb + e < nrows) & (lv[e] != kNegInf) & (sv[e] == kseq) &
+                           (pv[e] >= kpos);
+          const float pr = vis ? exp2_fast(fmaf(sacc[r], scale_log2, -lv[e])) : 0.f;
+          p[r] = pr;
+          ds[r] = pr * (dpacc[r] - dv4[e]);
+        }
       }
     }
     // dV^T += dO^T P, dK^T += Q^T dS  (k = 32 rows, 2 steps of 16).
@@ -442,21 +452,28 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
     for (int s2 = 0; s2 < 2; ++s2) {
       const bf16x8 pb = pack8(&p[8 * s2]);
       const bf16x8 db = pack8(&ds[8 * s2]);
+      if (!split) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8 at = tr_operand<D>(Ds, lo_off, 16 * s2, mb);
-        const bf16x8 aq = tr_operand<D>(Qs, lo_off, 16 * s2, mb);
-        dvacc[mb] = mfma32(at, pb, dvacc[mb]);
-        dkacc[mb] = mfma32(aq, db, dkacc[mb]);
-        if (split) {
-          float ph[8], dh[8];
+        for (int mb = 0; mb < MB; ++mb) {
+          dvacc[mb] = mfma32(tr_operand<D>(Ds, lo_off, 16 * s2, mb), pb, dvacc[mb]);
+          dkacc[mb] = mfma32(tr_operand<D>(Qs, lo_off, 16 * s2, mb), db, dkacc[mb]);
+        }
+      } else {
+        float ph[8], dh[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            ph[j] = p[8 * s2 + j] - static_cast<float>(pb[j]);
-            dh[j] = ds[8 * s2 + j] - static_cast<float>(db[j]);
-          }
-          dvacc[mb] = mfma32(at, pack8(ph), dvacc[mb]);
-          dkacc[mb] = mfma32(aq, pack8(dh), dkacc[mb]);
+        for (int j = 0; j < 8; ++j) {
+          ph[j] = p[8 * s2 + j] - static_cast<float>(pb[j]);
+          dh[j] = ds[8 * s2 + j] - static_cast<float>(db[j]);
+        }
+        const bf16x8 pl = pack8(ph), dl = pack8(dh);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const bf16x8 at = tr_operand<D>(Ds, lo_off, 16 * s2, mb);
+          const bf16x8 aq = tr_operand<D>(Qs, lo_off, 16 * s2, mb);
+          dvacc[mb] = mfma32(at, pb, dvacc[mb]);
+          dkacc[mb] = mfma32(aq, db, dkacc[mb]);
+          dvacc[mb] = mfma32(at, pl, dvacc[mb]);
+          dkacc[mb] = mfma32(aq, dl, dkacc[mb]);
         }
       }
     }

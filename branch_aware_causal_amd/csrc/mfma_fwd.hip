@@ -177,11 +177,12 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
         for (int ks = 0; ks < KS; ++ks)
           sacc[kb] = mfma32(row_operand<D>(Ks[b], lo_off, kb * 32, ks), qreg[ks], sacc[kb]);
       }
+      // raw scores; masked entries become -inf (scale > 0 keeps the max in place)
       float x[2][16];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[kb][r] = sacc[kb][r] * scale_log2;
+        for (int r = 0; r < 16; ++r) x[kb][r] = sacc[kb][r];
       if (!wave_full) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(x[kb][r], x[kb][r + 1]));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
       // lazy rescale: move the reference only when the tile max clears it by kRescale
       if (__any(mt > m_run + kRescale)) {
         const float m_new = fmaxf(m_run, mt);
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          x[kb][r] = exp2_fast(x[kb][r] - m_use);
+          x[kb][r] = exp2_fast(fmaf(x[kb][r], scale_log2, -m_use));
           l_run += x[kb][r];
         }
       // O^T += V^T P^T, four k-steps of 16 keys
