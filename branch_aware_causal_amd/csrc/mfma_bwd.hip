@@ -227,32 +227,48 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV: key-outer.  K and V of the workgroup's 128 keys stay in LDS; the
-// query rows that can see them stream through in tiles of 32 rows.
+// dK / dV: key-outer.  The workgroup owns 128 keys of one kv-head; the query
+// rows that can see them stream through in tiles of 64 rows.
+//
+// Eight waves, two per SIMD.  Wave w = (kw, rh) = (w % 4, w / 4):
+//   phase 1: P and dS for key group kw (32 keys, K and V held in registers)
+//            and tile rows 32*rh .. +31, written to LDS as packed bf16 MFMA
+//            operands;
+//   phase 2: dV^T += dO^T P and dK^T += Q^T dS for key group kw, head-dim
+//            columns [rh*D/2, (rh+1)*D/2), over all 64 rows of the tile (the
+//            partner wave's P / dS come from LDS).
+// So each wave keeps accumulators for only half the head dimension and the
+// two waves of a SIMD alternate MFMA with their softmax-gradient VALU work.
 //
 // Query tiles are visited from the END of the visible range backwards: every
 // key block of a sequence sees the same trailing rows, so the workgroups that
 // an XCD runs together read the same tiles at nearly the same time and share
-// them through L2 (front-to-back, their start rows differ and they do not).
-// Tiles arrive by direct global->LDS loads through a ring of NSTAGE buffers,
-// issued three tiles ahead with one barrier per tile.  Each stage is its own
-// __shared__ array so the compiler can tell the in-flight loads of one stage
-// from the reads of another and does not drain the whole pipeline.
+// them through L2.  Tiles arrive by direct global->LDS loads into a two-stage
+// ring, the next tile loading while the current one is computed.
 // ---------------------------------------------------------------------------
 namespace bwdkv {
-constexpr int NW = 4;          // waves per workgroup, 32 keys each
-constexpr int KB = NW * 32;    // keys per workgroup
-constexpr int NSTAGE = 4;      // tile buffers in the load ring
+constexpr int NW = 8;          // waves per workgroup
+constexpr int KB = 128;        // keys per workgroup (4 key groups of 32)
+constexpr int TR = 64;         // query rows per tile (2 halves of 32)
 constexpr float kSplitP = 1.f / 256.f;
-// s_waitcnt immediate that waits until at most n vector-memory ops are
-// outstanding (gfx9 encoding; expcnt / lgkmcnt left at their maxima).
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0xF70; }
 }  // namespace bwdkv
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14])
+constexpr int kWaitAll = 0;
+constexpr int kWaitLgkm = 0xC07F;   // lgkmcnt(0), vmcnt and expcnt not waited on
+
+template <int kWait>
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWait);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int D, int G>
-__global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
+__global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int nq, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ k_seq,
@@ -260,20 +276,20 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
     const uint16_t* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv) {
   using namespace bwdkv;
-  constexpr int TPT = 32 / G;          // tokens per 32-row query tile
+  constexpr int TPT = TR / G;               // tokens per tile
   constexpr int KS = D / 16;
-  constexpr int MB = D / 32;
+  constexpr int MH = D / 64;                // 32-column blocks per head-dim half
   constexpr int CPR = D / 8;
-  constexpr int KLOADS = KB * CPR / 256;    // 16-byte chunks per thread for the K / V block
-  constexpr int QROUNDS = 32 * CPR / 256;   // 16-byte DMA rounds per thread per tensor per tile
-  constexpr int PER_TILE = 2 * QROUNDS + 1; // DMA ops per thread per tile (Q, dO, one meta array)
+  constexpr int QROUNDS = TR * CPR / 512;   // 16-byte DMA rounds per thread per tensor per tile
 
-  __shared__ __attribute__((aligned(16))) uint16_t Kw[KB * D];     // keys x d, swizzled
-  __shared__ __attribute__((aligned(16))) uint16_t Vw[KB * D];
-  // tile ring: rows x d (swizzled) for Q and dO; meta = lse | delta | seq | pos, 64 words each
-  __shared__ __attribute__((aligned(16))) uint16_t Q0[32 * D], Q1[32 * D], Q2[32 * D], Q3[32 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t O0[32 * D], O1[32 * D], O2[32 * D], O3[32 * D];
-  __shared__ __attribute__((aligned(16))) uint32_t M0s[256], M1s[256], M2s[256], M3s[256];
+  // two-stage ring: rows x d (swizzled) for Q and dO; meta = lse | delta | seq | pos
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[TR * D], Q1[TR * D];
+  __shared__ __attribute__((aligned(16))) uint16_t O0[TR * D], O1[TR * D];
+  __shared__ __attribute__((aligned(16))) uint32_t M0s[4 * TR], M1s[4 * TR];
+  // P / dS exchange, MFMA B-operand layout: [wave][k-step][lane] x 8 bf16
+  __shared__ __attribute__((aligned(16))) bf16x8 Xp[NW * 2 * 64], Xd[NW * 2 * 64];
+  __shared__ __attribute__((aligned(16))) bf16x8 Xpl[NW * 2 * 64], Xdl[NW * 2 * 64];
+  __shared__ int Xf[NW];    // 0: no visible pair, 1: hi only, 2: hi + lo
 
   const float scale_log2 = scale * kLog2e;
   const int nblk = (nk + KB - 1) / KB;
@@ -283,78 +299,63 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
   const int key0 = kblk * KB;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
+  const int kw = wave & 3, rh = wave >> 2;   // key group, row half (phase 1) / column half (phase 2)
   const int n = lane & 31, hi = lane >> 5;
   const LaneOffsets<D> lo_off(lane);
+  // transposed-operand offsets of this wave's head-dim half (selected, not
+  // indexed, so that they stay in registers)
+  int trh[MH][2];
+#pragma unroll
+  for (int m = 0; m < MH; ++m)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) trh[m][e] = rh ? lo_off.tr[MH + m][e] : lo_off.tr[m][e];
 
-  // this lane's key (column n of the wave's 32-key block)
-  const int my_key = key0 + wave * 32 + n;
+  // this lane's key (column n of the wave's 32-key group)
+  const int my_key = key0 + kw * 32 + n;
   const bool key_valid = my_key < nk;
   const int kseq = key_valid ? k_seq[my_key] : INT_MIN;
   const int kpos = key_valid ? k_pos[my_key] : INT_MAX;
-  const int wk0 = key0 + wave * 32;
+  const int wk0 = key0 + kw * 32;
   const bool wave_valid = wk0 < nk;
   const int wkl = min(nk, wk0 + 32) - 1;
   const bool wave_complete = wk0 + 32 <= nk;
   const int wf_seq = wave_valid ? k_seq[wk0] : 0, wf_pos = wave_valid ? k_pos[wk0] : 0;
   const int wl_seq = wave_valid ? k_seq[wkl] : 0, wl_pos = wave_valid ? k_pos[wkl] : 0;
 
-  // K and V of the block into LDS
+  // K and V rows of the lane's key as MFMA B operands (k-elements 16*ks + 8*hi ..)
+  bf16x8 kreg[KS], vreg[KS];
+  {
+    const size_t kb = (static_cast<size_t>(key_valid ? my_key : 0) * hkv + g) * D + 8 * hi;
 #pragma unroll
-  for (int it = 0; it < KLOADS; ++it) {
-    const int c = tid + 256 * it;
-    const int kr = c / CPR, col = (c % CPR) * 8;
-    const int j = key0 + kr;
-    uint4 kk = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-    if (j < nk) {
-      const size_t off = (static_cast<size_t>(j) * hkv + g) * D + col;
-      kk = *reinterpret_cast<const uint4*>(k + off);
-      vv = *reinterpret_cast<const uint4*>(v + off);
+    for (int ks = 0; ks < KS; ++ks) {
+      kreg[ks] = key_valid ? *reinterpret_cast<const bf16x8*>(k + kb + 16 * ks) : zero8();
+      vreg[ks] = key_valid ? *reinterpret_cast<const bf16x8*>(v + kb + 16 * ks) : zero8();
     }
-    *reinterpret_cast<uint4*>(&Kw[toff<D>(kr, col)]) = kk;
-    *reinterpret_cast<uint4*>(&Vw[toff<D>(kr, col)]) = vv;
   }
-  __syncthreads();
 
-  // query tokens that can see any key of the block; tiles are taken from the
-  // end: tile i covers tokens [qhi - (i+1)*TPT, qhi - i*TPT) clipped at qlo
+  // query tokens that can see any key of the block; tile i covers tokens
+  // [qhi - (i+1)*TPT, qhi - i*TPT) clipped at qlo
   const int klast = min(nk, key0 + KB) - 1;
   const int qlo = lower_bound_sp(q_seq, q_pos, nq, k_seq[key0], k_pos[key0]);
   const int qhi = upper_bound_sp(q_seq, q_pos, nq, k_seq[klast], INT_MAX);
   const int ntiles = qhi > qlo ? (qhi - qlo + TPT - 1) / TPT : 0;
 
-  f32x16 dkacc[MB], dvacc[MB];
+  f32x16 dkacc[MH], dvacc[MH];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    dkacc[mb] = zero16();
-    dvacc[mb] = zero16();
+  for (int m = 0; m < MH; ++m) {
+    dkacc[m] = zero16();
+    dvacc[m] = zero16();
   }
 
-  auto qbuf = [&](auto S) -> uint16_t* {
-    if constexpr (S == 0) return Q0; else if constexpr (S == 1) return Q1;
-    else if constexpr (S == 2) return Q2; else return Q3;
-  };
-  auto obuf = [&](auto S) -> uint16_t* {
-    if constexpr (S == 0) return O0; else if constexpr (S == 1) return O1;
-    else if constexpr (S == 2) return O2; else return O3;
-  };
-  auto mbuf = [&](auto S) -> uint32_t* {
-    if constexpr (S == 0) return M0s; else if constexpr (S == 1) return M1s;
-    else if constexpr (S == 2) return M2s; else return M3s;
-  };
-
-  // First token of tile i (tiles taken from the end of [qlo, qhi)).
   auto tile_t0 = [&](int i) { return max(qlo, qhi - (i + 1) * TPT); };
 
-  // Issue the loads of tile i into stage S.  Lane l of round `it` of wave w
-  // fills 16-byte slot (it*NW + w)*64 + l of the tile, i.e. physical chunk p of
-  // row r; it fetches logical chunk swz(r, p) (the swizzle is an involution).
-  // Rows past the tile's end re-read its last row; they are masked by index.
-  auto issue = [&](auto S, int i) {
-    uint16_t* qd = qbuf(S);
-    uint16_t* od = obuf(S);
-    uint32_t* md = mbuf(S);
+  // Loads of tile i into one ring stage.  Lane l of round `it` of wave w fills
+  // 16-byte slot (it*NW + w)*64 + l of the tile, i.e. physical chunk p of row r;
+  // it fetches logical chunk swz(r, p) (the swizzle is an involution).  Rows
+  // past the tile's end re-read its last row; they are masked by index.
+  auto issue = [&](uint16_t* qd, uint16_t* od, uint32_t* md, int i) {
     const int t0 = tile_t0(i);
-    const int t1 = qhi - i * TPT;              // one past the tile's last token
+    const int t1 = qhi - i * TPT;
 #pragma unroll
     for (int it = 0; it < QROUNDS; ++it) {
       const int slot = (it * NW + wave) * 64 + lane;
@@ -367,8 +368,8 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
       __builtin_amdgcn_global_load_lds(q + off, (lds_void*)(qd + base), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(dout + off, (lds_void*)(od + base), 16, 0, 0);
     }
-    {
-      const int r = lane & 31;
+    if (wave < 4) {
+      const int r = lane;                      // TR == 64 rows, one per lane
       const int tok = min(t0 + r / G, t1 - 1);
       const int head = g * G + r % G;
       const size_t li = static_cast<size_t>(head) * nq + tok;
@@ -376,155 +377,165 @@ __global__ __launch_bounds__(256, 1) void main_bwd_dkdv_kernel(
                       : wave == 1 ? static_cast<const void*>(delta + li)
                       : wave == 2 ? static_cast<const void*>(q_seq + tok)
                                   : static_cast<const void*>(q_pos + tok);
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(md + wave * 64), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(md + wave * TR), 4, 0, 0);
     }
   };
 
-  auto compute = [&](auto S, int i) {
-    const uint16_t* Qs = qbuf(S);
-    const uint16_t* Ds = obuf(S);
-    const uint32_t* M = mbuf(S);
+  // Phase 1: P and dS of (key group kw, rows 32*rh ..) into the exchange.
+  auto phase1 = [&](const uint16_t* Qs, const uint16_t* Ds, const uint32_t* M, int i) {
     const float* lse_s = reinterpret_cast<const float*>(M);
-    const float* dl_s = reinterpret_cast<const float*>(M + 64);
-    const int* rseq_s = reinterpret_cast<const int*>(M + 128);
-    const int* rpos_s = reinterpret_cast<const int*>(M + 192);
+    const float* dl_s = reinterpret_cast<const float*>(M + TR);
+    const int* rseq_s = reinterpret_cast<const int*>(M + 2 * TR);
+    const int* rpos_s = reinterpret_cast<const int*>(M + 3 * TR);
     const int t0 = tile_t0(i);
     const int nrows = (qhi - i * TPT - t0) * G;   // valid rows of this tile
-    const int rl = nrows - 1;
-    const int rf_seq = rseq_s[0], rf_pos = rpos_s[0];
-    const int rl_seq = rseq_s[rl], rl_pos = rpos_s[rl];
-    const bool wave_any = wave_valid && !lex_less(rl_seq, rl_pos, wf_seq, wf_pos) &&
-                          !lex_less(wl_seq, INT_MAX, rf_seq, rf_pos);
-    const bool wave_full = wave_complete && rl == 31 && rf_seq == rl_seq && rf_seq == wf_seq &&
-                           wf_seq == wl_seq && rf_pos >= wl_pos;
-    if (!wave_any) return;
-    // S = Q K^T, dP = dO V^T: lane (n = key, hi) register r holds row acc_row(r, hi)
-    f32x16 sacc = zero16(), dpacc = zero16();
+    const int r0 = 32 * rh;                       // this wave's first row
+    int flag = 0;
+    if (r0 < nrows) {
+      const int rl = min(nrows, r0 + 32) - 1;
+      const int rf_seq = rseq_s[r0], rf_pos = rpos_s[r0];
+      const int rl_seq = rseq_s[rl], rl_pos = rpos_s[rl];
+      const bool wave_any = wave_valid && !lex_less(rl_seq, rl_pos, wf_seq, wf_pos) &&
+                            !lex_less(wl_seq, INT_MAX, rf_seq, rf_pos);
+      const bool wave_full = wave_complete && rl == r0 + 31 && rf_seq == rl_seq &&
+                             rf_seq == wf_seq && wf_seq == wl_seq && rf_pos >= wl_pos;
+      if (wave_any) {
+        // S = Q K^T, dP = dO V^T: lane (n = key, hi) register r holds row r0 + acc_row(r, hi)
+        f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      sacc = mfma32(row_operand<D>(Qs, lo_off, 0, ks), row_operand<D>(Kw, lo_off, wave * 32, ks), sacc);
-      dpacc = mfma32(row_operand<D>(Ds, lo_off, 0, ks), row_operand<D>(Vw, lo_off, wave * 32, ks), dpacc);
-    }
-    float p[16], ds[16];
+        for (int ks = 0; ks < KS; ++ks) sacc = mfma32(row_operand<D>(Qs, lo_off, r0, ks), kreg[ks], sacc);
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int rb = 8 * r4 + 4 * hi;
-      const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[rb]);
-      const float4 d4 = *reinterpret_cast<const float4*>(&dl_s[rb]);
-      const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
-      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-      if (wave_full) {
-        // every row valid and every key visible: no mask
+        for (int ks = 0; ks < KS; ++ks) dpacc = mfma32(row_operand<D>(Ds, lo_off, r0, ks), vreg[ks], dpacc);
+        float p[16], ds[16];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          p[r] = exp2_fast(fmaf(sacc[r], scale_log2, -lv[e]));
-          ds[r] = p[r] * (dpacc[r] - dv4[e]);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int rb = r0 + 8 * r4 + 4 * hi;
+          const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[rb]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&dl_s[rb]);
+          const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+          if (wave_full) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * r4 + e;
+              p[r] = exp2_fast(fmaf(sacc[r], scale_log2, -lv[e]));
+              ds[r] = p[r] * (dpacc[r] - dv4[e]);
+            }
+          } else {
+            const int4 ss = *reinterpret_cast<const int4*>(&rseq_s[rb]);
+            const int4 pp = *reinterpret_cast<const int4*>(&rpos_s[rb]);
+            const int sv[4] = {ss.x, ss.y, ss.z, ss.w};
+            const int pv[4] = {pp.x, pp.y, pp.z, pp.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * r4 + e;
+              const bool vis = key_valid & (rb + e < nrows) & (lv[e] != kNegInf) &
+                               (sv[e] == kseq) & (pv[e] >= kpos);
+              const float pr = vis ? exp2_fast(fmaf(sacc[r], scale_log2, -lv[e])) : 0.f;
+              p[r] = pr;
+              ds[r] = pr * (dpacc[r] - dv4[e]);
+            }
+          }
         }
-      } else {
-        const int4 ss = *reinterpret_cast<const int4*>(&rseq_s[rb]);
-        const int4 pp = *reinterpret_cast<const int4*>(&rpos_s[rb]);
-        const int sv[4] = {ss.x, ss.y, ss.z, ss.w};
-        const int pv[4] = {pp.x, pp.y, pp.z, pp.w};
+        // P and dS enter the gradient MFMAs as bf16.  Where some P of the
+        // block reaches kSplitP they enter as hi + lo bf16 pairs (lo = x - hi,
+        // a second MFMA on the same A operand): rows that give a key a large
+        // weight would otherwise carry bf16's 2^-9 relative rounding into the
+        // key's gradient with a large coefficient.  Below the threshold the
+        // dropped lo terms are at most kSplitP * 2^-9 each.
+        bool big = false;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          const bool vis = key_valid & (rb + e < nrows) & (lv[e] != kNegInf) & (sv[e] == kseq) &
-                           (pv[e] >= kpos);
-          const float pr = vis ? exp2_fast(fmaf(sacc[r], scale_log2, -lv[e])) : 0.f;
-          p[r] = pr;
-          ds[r] = pr * (dpacc[r] - dv4[e]);
+        for (int r = 0; r < 16; ++r) big |= p[r] >= kSplitP;
+        const bool split = __any(big);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const bf16x8 pb = pack8(&p[8 * s2]);
+          const bf16x8 db = pack8(&ds[8 * s2]);
+          Xp[(wave * 2 + s2) * 64 + lane] = pb;
+          Xd[(wave * 2 + s2) * 64 + lane] = db;
+          if (split) {
+            float ph[8], dh[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              ph[j] = p[8 * s2 + j] - static_cast<float>(pb[j]);
+              dh[j] = ds[8 * s2 + j] - static_cast<float>(db[j]);
+            }
+            Xpl[(wave * 2 + s2) * 64 + lane] = pack8(ph);
+            Xdl[(wave * 2 + s2) * 64 + lane] = pack8(dh);
+          }
         }
+        flag = split ? 2 : 1;
       }
     }
-    // dV^T += dO^T P, dK^T += Q^T dS  (k = 32 rows, 2 steps of 16).
-    // P and dS enter the MFMA as bf16.  Where some P of the block reaches
-    // kSplitP they enter as hi + lo bf16 pairs (lo = x - hi, a second MFMA on
-    // the same A operand): rows that give a key a large weight would otherwise
-    // carry bf16's 2^-9 relative rounding into the key's gradient with a large
-    // coefficient.  Below the threshold the dropped lo terms are at most
-    // kSplitP * 2^-9 each.
-    bool big = false;
+    if (lane == 0) Xf[wave] = flag;
+  };
+
+  // Phase 2: dV^T / dK^T columns of this wave's half over the tile's 64 rows.
+  // Rows 32*h + 16*s2 + 8*(j/4) + 4*hi + (j%4) are k-element j of k-step
+  // (h, s2): the register order of the P / dS packs written in phase 1.
+  auto phase2 = [&](const uint16_t* Qs, const uint16_t* Ds) {
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {
+      const int f = __builtin_amdgcn_readfirstlane(Xf[kw + 4 * h]);
+      if (f == 0) continue;
+      const int src = (kw + 4 * h) * 2;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) big |= p[r] >= kSplitP;
-    const bool split = __any(big);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8 pb = Xp[(src + s2) * 64 + lane];
+        const bf16x8 db = Xd[(src + s2) * 64 + lane];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const bf16x8 pb = pack8(&p[8 * s2]);
-      const bf16x8 db = pack8(&ds[8 * s2]);
-      if (!split) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          dvacc[mb] = mfma32(tr_operand<D>(Ds, lo_off, 16 * s2, mb), pb, dvacc[mb]);
-          dkacc[mb] = mfma32(tr_operand<D>(Qs, lo_off, 16 * s2, mb), db, dkacc[mb]);
-        }
-      } else {
-        float ph[8], dh[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          ph[j] = p[8 * s2 + j] - static_cast<float>(pb[j]);
-          dh[j] = ds[8 * s2 + j] - static_cast<float>(db[j]);
-        }
-        const bf16x8 pl = pack8(ph), dl = pack8(dh);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const bf16x8 at = tr_operand<D>(Ds, lo_off, 16 * s2, mb);
-          const bf16x8 aq = tr_operand<D>(Qs, lo_off, 16 * s2, mb);
-          dvacc[mb] = mfma32(at, pb, dvacc[mb]);
-          dkacc[mb] = mfma32(aq, db, dkacc[mb]);
-          dvacc[mb] = mfma32(at, pl, dvacc[mb]);
-          dkacc[mb] = mfma32(aq, dl, dkacc[mb]);
+        for (int m = 0; m < MH; ++m) {
+          const bf16x8 at = tr_operand_at<D>(Ds, 32 * h + 16 * s2, trh[m][0], trh[m][1]);
+          const bf16x8 aq = tr_operand_at<D>(Qs, 32 * h + 16 * s2, trh[m][0], trh[m][1]);
+          dvacc[m] = mfma32(at, pb, dvacc[m]);
+          dkacc[m] = mfma32(aq, db, dkacc[m]);
+          if (f == 2) {
+            dvacc[m] = mfma32(at, Xpl[(src + s2) * 64 + lane], dvacc[m]);
+            dkacc[m] = mfma32(aq, Xdl[(src + s2) * 64 + lane], dkacc[m]);
+          }
         }
       }
     }
   };
 
-  // One tile: wait until its loads are done (the two later tiles' loads may
-  // still be in flight), barrier (all waves' loads visible; every wave is done
-  // with the stage about to be refilled), refill that stage three tiles
-  // ahead, compute.
-  auto step = [&](auto S, int i) {
-    const int ahead = min(2, ntiles - 1 - i);
-    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * PER_TILE));
-    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_TILE));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    __builtin_amdgcn_s_barrier();
-    if (i + 3 < ntiles) issue(std::integral_constant<int, (S + 3) % NSTAGE>{}, i + 3);
-    compute(S, i);
-  };
-
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  if (ntiles > 0) issue(I0{}, 0);
-  if (ntiles > 1) issue(I1{}, 1);
-  if (ntiles > 2) issue(I2{}, 2);
-  for (int i = 0; i < ntiles; i += NSTAGE) {
-    step(I0{}, i);
-    if (i + 1 < ntiles) step(I1{}, i + 1);
-    if (i + 2 < ntiles) step(I2{}, i + 2);
-    if (i + 3 < ntiles) step(I3{}, i + 3);
+  // Per tile: wait for its loads (the only ones in flight) and barrier (data
+  // visible; every wave done with the previous tile's stage and exchange),
+  // start loading the next tile into the other stage, phase 1, barrier
+  // (exchange written), phase 2.
+  if (ntiles > 0) issue(Q0, O0, M0s, 0);
+  for (int i = 0; i < ntiles; i += 2) {
+    wg_barrier<kWaitAll>();
+    if (i + 1 < ntiles) issue(Q1, O1, M1s, i + 1);
+    phase1(Q0, O0, M0s, i);
+    wg_barrier<kWaitLgkm>();
+    phase2(Q0, O0);
+    if (i + 1 < ntiles) {
+      wg_barrier<kWaitAll>();
+      if (i + 2 < ntiles) issue(Q0, O0, M0s, i + 2);
+      phase1(Q1, O1, M1s, i + 1);
+      wg_barrier<kWaitLgkm>();
+      phase2(Q1, O1);
+    }
   }
 
   if (!key_valid) return;
   const size_t obase = (static_cast<size_t>(my_key) * hkv + g) * D;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int m = 0; m < MH; ++m)
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      const size_t off = obase + mb * 32 + 8 * gq + 4 * hi;
+      const size_t off = obase + (rh * MH + m) * 32 + 8 * gq + 4 * hi;
       float4* pk = reinterpret_cast<float4*>(dk + off);
       float4* pv = reinterpret_cast<float4*>(dv + off);
       float4 a = *pk, c = *pv;
-      a.x += scale * dkacc[mb][4 * gq + 0];
-      a.y += scale * dkacc[mb][4 * gq + 1];
-      a.z += scale * dkacc[mb][4 * gq + 2];
-      a.w += scale * dkacc[mb][4 * gq + 3];
-      c.x += dvacc[mb][4 * gq + 0];
-      c.y += dvacc[mb][4 * gq + 1];
-      c.z += dvacc[mb][4 * gq + 2];
-      c.w += dvacc[mb][4 * gq + 3];
+      a.x += scale * dkacc[m][4 * gq + 0];
+      a.y += scale * dkacc[m][4 * gq + 1];
+      a.z += scale * dkacc[m][4 * gq + 2];
+      a.w += scale * dkacc[m][4 * gq + 3];
+      c.x += dvacc[m][4 * gq + 0];
+      c.y += dvacc[m][4 * gq + 1];
+      c.z += dvacc[m][4 * gq + 2];
+      c.w += dvacc[m][4 * gq + 3];
       *pk = a;
       *pv = c;
     }
@@ -543,7 +554,7 @@ static void main_bwd_mfma_dg(const MainArgs& a, int part) {
   }
   if (part != 1) {
     const int nblk = (a.nk + bwdkv::KB - 1) / bwdkv::KB;
-    hipLaunchKernelGGL((main_bwd_dkdv_kernel<D, G>), dim3(nblk * a.hkv), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((main_bwd_dkdv_kernel<D, G>), dim3(nblk * a.hkv), dim3(512), 0, a.stream,
                        static_cast<const uint16_t*>(a.q), a.q_seq, a.q_pos, a.nq,
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                        a.k_seq, a.k_pos, a.nk, a.hq, a.hkv, a.scale,

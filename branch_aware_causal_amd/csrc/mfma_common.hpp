@@ -119,6 +119,19 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, const LaneOff
   return r;
 }
 
+// Transposed operand from precomputed lane offsets (LaneOffsets::tr[mb]).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand_at(const uint16_t* tile, int kbase, int off0, int off1) {
+  lds_bf16x4* p0 = (lds_bf16x4*)(tile + kbase * D + off0);
+  lds_bf16x4* p1 = (lds_bf16x4*)(tile + kbase * D + off1);
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p0);
+  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p1);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
 // Accumulator row of register r for lane half hi.
 __device__ __forceinline__ int acc_row(int r, int hi) { return 8 * (r >> 2) + 4 * hi + (r & 3); }
 
