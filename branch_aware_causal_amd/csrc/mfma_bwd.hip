@@ -19,7 +19,6 @@
 // is race-free within a launch and ordered across launches on one stream.
 
 #include <climits>
-#include <type_traits>
 
 #include "launch.hpp"
 #include "mfma_common.hpp"
@@ -231,20 +230,24 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
 // rows that can see them stream through in tiles of 64 rows.
 //
 // Eight waves, two per SIMD.  Wave w = (kw, rh) = (w % 4, w / 4):
-//   phase 1: P and dS for key group kw (32 keys, K and V held in registers)
-//            and tile rows 32*rh .. +31, written to LDS as packed bf16 MFMA
-//            operands;
-//   phase 2: dV^T += dO^T P and dK^T += Q^T dS for key group kw, head-dim
-//            columns [rh*D/2, (rh+1)*D/2), over all 64 rows of the tile (the
-//            partner wave's P / dS come from LDS).
-// So each wave keeps accumulators for only half the head dimension and the
-// two waves of a SIMD alternate MFMA with their softmax-gradient VALU work.
+//   * for tile rows 32*rh .. +31 and key group kw (32 keys; K and V held in
+//     registers) it computes S, dP, P and dS;
+//   * the wave with rh = 0 accumulates dV^T = dO^T P and the one with rh = 1
+//     dK^T = Q^T dS for the key group, each over the tile's 64 rows and the
+//     full head dimension.  The partner's half of P (or dS) arrives through
+//     LDS as packed bf16 MFMA operands.
+//
+// Software pipeline (one iteration per tile i, two barriers): the S / dP
+// MFMAs of tile i go to the matrix core before the exchange barrier; after
+// it, the dV / dK MFMAs of tile i-1 run while the same wave computes the
+// softmax gradient of tile i on the vector ALUs.  Q / dO tiles arrive by
+// direct global->LDS loads into a three-stage ring (tile i+1 loading, i in
+// the S / dP step, i-1 in the dV / dK step).
 //
 // Query tiles are visited from the END of the visible range backwards: every
 // key block of a sequence sees the same trailing rows, so the workgroups that
 // an XCD runs together read the same tiles at nearly the same time and share
-// them through L2.  Tiles arrive by direct global->LDS loads into a two-stage
-// ring, the next tile loading while the current one is computed.
+// them through L2.
 // ---------------------------------------------------------------------------
 namespace bwdkv {
 constexpr int NW = 8;          // waves per workgroup
@@ -267,6 +270,25 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// 32-bit LDS address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)p));
+}
+
+// Direct global->LDS loads: lane l writes LDS[lds + l*bytes].  Issued as
+// inline assembly so that the compiler does not guard later LDS reads with
+// waits on these loads: the kernel waits for them itself (vmcnt) before the
+// barrier that publishes a ring stage.  `lds` must be wave-uniform.  The
+// s_nop covers the M0 write -> LDS-DMA hazard.
+__device__ __forceinline__ void dma_b128(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(g), "s"(lds) : "memory", "m0");
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ q_seq,
@@ -278,18 +300,20 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
   using namespace bwdkv;
   constexpr int TPT = TR / G;               // tokens per tile
   constexpr int KS = D / 16;
-  constexpr int MH = D / 64;                // 32-column blocks per head-dim half
+  constexpr int MB = D / 32;
   constexpr int CPR = D / 8;
+  constexpr int TS = TR * D;                // elements of one tensor tile
   constexpr int QROUNDS = TR * CPR / 512;   // 16-byte DMA rounds per thread per tensor per tile
+  constexpr int XN = NW * 2 * 64;           // packs per exchange buffer
 
-  // two-stage ring: rows x d (swizzled) for Q and dO; meta = lse | delta | seq | pos
-  __shared__ __attribute__((aligned(16))) uint16_t Q0[TR * D], Q1[TR * D];
-  __shared__ __attribute__((aligned(16))) uint16_t O0[TR * D], O1[TR * D];
-  __shared__ __attribute__((aligned(16))) uint32_t M0s[4 * TR], M1s[4 * TR];
-  // P / dS exchange, MFMA B-operand layout: [wave][k-step][lane] x 8 bf16
-  __shared__ __attribute__((aligned(16))) bf16x8 Xp[NW * 2 * 64], Xd[NW * 2 * 64];
-  __shared__ __attribute__((aligned(16))) bf16x8 Xpl[NW * 2 * 64], Xdl[NW * 2 * 64];
-  __shared__ int Xf[NW];    // 0: no visible pair, 1: hi only, 2: hi + lo
+  // three-stage ring; a stage holds Q | dO (rows x d, swizzled) and
+  // meta = lse | delta | seq | pos of its 64 rows
+  __shared__ __attribute__((aligned(16))) uint16_t R[3][2 * TS];
+  __shared__ __attribute__((aligned(16))) uint32_t Mr[3][4 * TR];
+  // partner-bound packs, MFMA B-operand layout: [wave][k-step][lane] x 8 bf16;
+  // hi parts double-buffered by tile parity, lo parts single-buffered
+  __shared__ __attribute__((aligned(16))) bf16x8 Xh[2 * XN], Xl[XN];
+  __shared__ int Xf[2 * NW];    // 0: nothing visible, 1: hi only, 2: hi + lo
 
   const float scale_log2 = scale * kLog2e;
   const int nblk = (nk + KB - 1) / KB;
@@ -299,16 +323,10 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
   const int key0 = kblk * KB;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int kw = wave & 3, rh = wave >> 2;   // key group, row half (phase 1) / column half (phase 2)
+  const int kw = wave & 3, rh = wave >> 2;   // key group; row half and role (0: dV, 1: dK)
+  const int partner = wave ^ 4;
   const int n = lane & 31, hi = lane >> 5;
   const LaneOffsets<D> lo_off(lane);
-  // transposed-operand offsets of this wave's head-dim half (selected, not
-  // indexed, so that they stay in registers)
-  int trh[MH][2];
-#pragma unroll
-  for (int m = 0; m < MH; ++m)
-#pragma unroll
-    for (int e = 0; e < 2; ++e) trh[m][e] = rh ? lo_off.tr[MH + m][e] : lo_off.tr[m][e];
 
   // this lane's key (column n of the wave's 32-key group)
   const int my_key = key0 + kw * 32 + n;
@@ -340,20 +358,23 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
   const int qhi = upper_bound_sp(q_seq, q_pos, nq, k_seq[klast], INT_MAX);
   const int ntiles = qhi > qlo ? (qhi - qlo + TPT - 1) / TPT : 0;
 
-  f32x16 dkacc[MH], dvacc[MH];
+  f32x16 acc[MB];   // dV^T (rh = 0) or dK^T (rh = 1): rows = head-dim columns, cols = keys
 #pragma unroll
-  for (int m = 0; m < MH; ++m) {
-    dkacc[m] = zero16();
-    dvacc[m] = zero16();
-  }
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = zero16();
+  // this wave's own packs (P for rh = 0, dS for rh = 1) of the previous tile.
+  // Every pack is defined on every path (zero where unused): the lo MFMAs are
+  // conditional, and undefined operands on the untaken side have let the
+  // compiler produce wrong accumulators.
+  bf16x8 own_h[2] = {zero8(), zero8()}, own_l[2] = {zero8(), zero8()};
+  int own_f = 0;
 
   auto tile_t0 = [&](int i) { return max(qlo, qhi - (i + 1) * TPT); };
 
-  // Loads of tile i into one ring stage.  Lane l of round `it` of wave w fills
+  // Loads of tile i into ring stage st.  Lane l of round `it` of wave w fills
   // 16-byte slot (it*NW + w)*64 + l of the tile, i.e. physical chunk p of row r;
   // it fetches logical chunk swz(r, p) (the swizzle is an involution).  Rows
   // past the tile's end re-read its last row; they are masked by index.
-  auto issue = [&](uint16_t* qd, uint16_t* od, uint32_t* md, int i) {
+  auto issue = [&](int st, int i) {
     const int t0 = tile_t0(i);
     const int t1 = qhi - i * TPT;
 #pragma unroll
@@ -364,9 +385,10 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
       const int tok = min(t0 + r / G, t1 - 1);
       const int head = g * G + r % G;
       const size_t off = (static_cast<size_t>(tok) * hq + head) * D + 8 * c;
-      const int base = (it * NW + wave) * 64 * 8;
-      __builtin_amdgcn_global_load_lds(q + off, (lds_void*)(qd + base), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(dout + off, (lds_void*)(od + base), 16, 0, 0);
+      const uint32_t base = __builtin_amdgcn_readfirstlane(
+          lds_addr(&R[st][(it * NW + wave) * 64 * 8]));
+      dma_b128(q + off, base);
+      dma_b128(dout + off, base + TS * 2);
     }
     if (wave < 4) {
       const int r = lane;                      // TR == 64 rows, one per lane
@@ -377,167 +399,207 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
                       : wave == 1 ? static_cast<const void*>(delta + li)
                       : wave == 2 ? static_cast<const void*>(q_seq + tok)
                                   : static_cast<const void*>(q_pos + tok);
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(md + wave * TR), 4, 0, 0);
+      dma_b32(src, __builtin_amdgcn_readfirstlane(lds_addr(&Mr[st][wave * TR])));
     }
   };
 
-  // Phase 1: P and dS of (key group kw, rows 32*rh ..) into the exchange.
-  auto phase1 = [&](const uint16_t* Qs, const uint16_t* Ds, const uint32_t* M, int i) {
+  // Iteration i: S / dP of tile i (stage sc), dV / dK of tile i-1 (stage sp),
+  // loads of tile i+1 into stage sn.  Iterations run 0 .. ntiles; the last
+  // one only finishes tile ntiles-1.
+  if (ntiles > 0) issue(0, 0);
+  int sc = 0;
+  for (int i = 0; i <= ntiles; ++i) {
+    const int sn = sc == 2 ? 0 : sc + 1;
+    const int sp = sc == 0 ? 2 : sc - 1;
+    const uint16_t* const cur = R[sc];
+    const uint16_t* const prv = R[sp];
+    const uint32_t* const M = Mr[sc];
+
+    // tile i landed; X and Xf hold tile i-1's partner packs; stage sn is free
+    wg_barrier<kWaitAll>();
+    if (i + 1 < ntiles) issue(sn, i + 1);
+
+    // partner packs of tile i-1: hi parts are read where they are used (their
+    // buffer is not rewritten before iteration i+1), lo parts now (the single
+    // lo buffer is rewritten after the next barrier)
+    const int xo_prv = (i + 1) & 1, xo_cur = i & 1;
+    int par_f = 0;
+    bf16x8 par_l[2] = {zero8(), zero8()};
+    if (i >= 1) {
+      par_f = __builtin_amdgcn_readfirstlane(Xf[xo_prv * NW + partner]);
+      if (par_f == 2) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) par_l[s2] = Xl[(partner * 2 + s2) * 64 + lane];
+      }
+    }
+
+    // S = Q K^T, dP = dO V^T of tile i: lane (n = key, hi) register r holds
+    // row r0 + acc_row(r, hi)
     const float* lse_s = reinterpret_cast<const float*>(M);
     const float* dl_s = reinterpret_cast<const float*>(M + TR);
     const int* rseq_s = reinterpret_cast<const int*>(M + 2 * TR);
     const int* rpos_s = reinterpret_cast<const int*>(M + 3 * TR);
-    const int t0 = tile_t0(i);
-    const int nrows = (qhi - i * TPT - t0) * G;   // valid rows of this tile
-    const int r0 = 32 * rh;                       // this wave's first row
-    int flag = 0;
-    if (r0 < nrows) {
-      const int rl = min(nrows, r0 + 32) - 1;
-      const int rf_seq = rseq_s[r0], rf_pos = rpos_s[r0];
-      const int rl_seq = rseq_s[rl], rl_pos = rpos_s[rl];
-      const bool wave_any = wave_valid && !lex_less(rl_seq, rl_pos, wf_seq, wf_pos) &&
-                            !lex_less(wl_seq, INT_MAX, rf_seq, rf_pos);
-      const bool wave_full = wave_complete && rl == r0 + 31 && rf_seq == rl_seq &&
-                             rf_seq == wf_seq && wf_seq == wl_seq && rf_pos >= wl_pos;
-      if (wave_any) {
-        // S = Q K^T, dP = dO V^T: lane (n = key, hi) register r holds row r0 + acc_row(r, hi)
-        f32x16 sacc = zero16(), dpacc = zero16();
+    const int r0 = 32 * rh;
+    bool active = false, wave_full = false;
+    int nrows = 0;
+    f32x16 sacc = zero16(), dpacc = zero16();
+    if (i < ntiles) {
+      const int t0 = tile_t0(i);
+      nrows = (qhi - i * TPT - t0) * G;
+      if (r0 < nrows) {
+        const int rl = min(nrows, r0 + 32) - 1;
+        const int rf_seq = rseq_s[r0], rf_pos = rpos_s[r0];
+        const int rl_seq = rseq_s[rl], rl_pos = rpos_s[rl];
+        active = wave_valid && !lex_less(rl_seq, rl_pos, wf_seq, wf_pos) &&
+                 !lex_less(wl_seq, INT_MAX, rf_seq, rf_pos);
+        wave_full = wave_complete && rl == r0 + 31 && rf_seq == rl_seq && rf_seq == wf_seq &&
+                    wf_seq == wl_seq && rf_pos >= wl_pos;
+      }
+      if (active) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sacc = mfma32(row_operand<D>(Qs, lo_off, r0, ks), kreg[ks], sacc);
+        for (int ks = 0; ks < KS; ++ks)
+          sacc = mfma32(row_operand<D>(cur, lo_off, r0, ks), kreg[ks], sacc);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) dpacc = mfma32(row_operand<D>(Ds, lo_off, r0, ks), vreg[ks], dpacc);
-        float p[16], ds[16];
+        for (int ks = 0; ks < KS; ++ks)
+          dpacc = mfma32(row_operand<D>(cur + TS, lo_off, r0, ks), vreg[ks], dpacc);
+      }
+    }
+
+    // every wave has read its partner's lo packs
+    wg_barrier<kWaitLgkm>();
+
+    // dV^T += dO^T P (rh = 0) or dK^T += Q^T dS (rh = 1) over tile i-1's 64
+    // rows.  Rows 32*h + 16*s2 + 8*(j/4) + 4*hi + (j%4) are k-element j of
+    // k-step (h, s2): the register order of the packs.
+    auto gradients = [&]() {
+      if (i < 1) return;
+      const uint16_t* At = prv + (rh ? 0 : TS);
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int rb = r0 + 8 * r4 + 4 * hi;
-          const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[rb]);
-          const float4 d4 = *reinterpret_cast<const float4*>(&dl_s[rb]);
-          const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
-          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-          if (wave_full) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * r4 + e;
-              p[r] = exp2_fast(fmaf(sacc[r], scale_log2, -lv[e]));
-              ds[r] = p[r] * (dpacc[r] - dv4[e]);
-            }
-          } else {
-            const int4 ss = *reinterpret_cast<const int4*>(&rseq_s[rb]);
-            const int4 pp = *reinterpret_cast<const int4*>(&rpos_s[rb]);
-            const int sv[4] = {ss.x, ss.y, ss.z, ss.w};
-            const int pv[4] = {pp.x, pp.y, pp.z, pp.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * r4 + e;
-              const bool vis = key_valid & (rb + e < nrows) & (lv[e] != kNegInf) &
-                               (sv[e] == kseq) & (pv[e] >= kpos);
-              const float pr = vis ? exp2_fast(fmaf(sacc[r], scale_log2, -lv[e])) : 0.f;
-              p[r] = pr;
-              ds[r] = pr * (dpacc[r] - dv4[e]);
-            }
-          }
-        }
-        // P and dS enter the gradient MFMAs as bf16.  Where some P of the
-        // block reaches kSplitP they enter as hi + lo bf16 pairs (lo = x - hi,
-        // a second MFMA on the same A operand): rows that give a key a large
-        // weight would otherwise carry bf16's 2^-9 relative rounding into the
-        // key's gradient with a large coefficient.  Below the threshold the
-        // dropped lo terms are at most kSplitP * 2^-9 each.
-        bool big = false;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) big |= p[r] >= kSplitP;
-        const bool split = __any(big);
+      for (int h = 0; h < 2; ++h) {
+        const bool mine = h == rh;
+        const int f = mine ? own_f : par_f;
+        if (f == 0) continue;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const bf16x8 pb = pack8(&p[8 * s2]);
-          const bf16x8 db = pack8(&ds[8 * s2]);
-          Xp[(wave * 2 + s2) * 64 + lane] = pb;
-          Xd[(wave * 2 + s2) * 64 + lane] = db;
+          const bf16x8 bh = mine ? own_h[s2] : Xh[xo_prv * XN + (partner * 2 + s2) * 64 + lane];
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const bf16x8 a = tr_operand<D>(At, lo_off, 32 * h + 16 * s2, mb);
+            acc[mb] = mfma32(a, bh, acc[mb]);
+            if (f == 2) acc[mb] = mfma32(a, mine ? own_l[s2] : par_l[s2], acc[mb]);
+          }
+        }
+      }
+    };
+
+    // softmax gradient of tile i: P, dS; own packs into new_*, partner-bound
+    // packs into the exchange
+    bf16x8 new_h[2] = {zero8(), zero8()}, new_l[2] = {zero8(), zero8()};
+    int new_f = 0;
+    auto softmax = [&]() {
+      if (!active) return;
+      float p[16], ds[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int rb = r0 + 8 * r4 + 4 * hi;
+        const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[rb]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&dl_s[rb]);
+        const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        if (wave_full) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e;
+            p[r] = exp2_fast(fmaf(sacc[r], scale_log2, -lv[e]));
+            ds[r] = p[r] * (dpacc[r] - dv4[e]);
+          }
+        } else {
+          const int4 ss = *reinterpret_cast<const int4*>(&rseq_s[rb]);
+          const int4 pp = *reinterpret_cast<const int4*>(&rpos_s[rb]);
+          const int sv[4] = {ss.x, ss.y, ss.z, ss.w};
+          const int pv[4] = {pp.x, pp.y, pp.z, pp.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e;
+            const bool vis = key_valid & (rb + e < nrows) & (lv[e] != kNegInf) &
+                             (sv[e] == kseq) & (pv[e] >= kpos);
+            const float pr = vis ? exp2_fast(fmaf(sacc[r], scale_log2, -lv[e])) : 0.f;
+            p[r] = pr;
+            ds[r] = pr * (dpacc[r] - dv4[e]);
+          }
+        }
+      }
+      // P and dS enter the gradient MFMAs as bf16.  Where some P of the
+      // block reaches kSplitP they enter as hi + lo bf16 pairs (lo = x - hi,
+      // a second MFMA on the same A operand): rows that give a key a large
+      // weight would otherwise carry bf16's 2^-9 relative rounding into the
+      // key's gradient with a large coefficient.  Below the threshold the
+      // dropped lo terms are at most kSplitP * 2^-9 each.
+      bool big = false;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) big |= p[r] >= kSplitP;
+      const bool split = __any(big);
+      new_f = split ? 2 : 1;
+      // own: P (rh = 0) or dS (rh = 1); partner-bound: the other one
+      auto emit = [&](const float (&mine)[16], const float (&theirs)[16]) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const bf16x8 oh = pack8(&mine[8 * s2]);
+          const bf16x8 th = pack8(&theirs[8 * s2]);
+          new_h[s2] = oh;
+          Xh[xo_cur * XN + (wave * 2 + s2) * 64 + lane] = th;
           if (split) {
-            float ph[8], dh[8];
+            float ol[8], tl[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-              ph[j] = p[8 * s2 + j] - static_cast<float>(pb[j]);
-              dh[j] = ds[8 * s2 + j] - static_cast<float>(db[j]);
+              ol[j] = mine[8 * s2 + j] - static_cast<float>(oh[j]);
+              tl[j] = theirs[8 * s2 + j] - static_cast<float>(th[j]);
             }
-            Xpl[(wave * 2 + s2) * 64 + lane] = pack8(ph);
-            Xdl[(wave * 2 + s2) * 64 + lane] = pack8(dh);
+            new_l[s2] = pack8(ol);
+            Xl[(wave * 2 + s2) * 64 + lane] = pack8(tl);
           }
         }
-        flag = split ? 2 : 1;
-      }
-    }
-    if (lane == 0) Xf[wave] = flag;
-  };
+      };
+      if (rh) emit(ds, p);
+      else emit(p, ds);
+    };
 
-  // Phase 2: dV^T / dK^T columns of this wave's half over the tile's 64 rows.
-  // Rows 32*h + 16*s2 + 8*(j/4) + 4*hi + (j%4) are k-element j of k-step
-  // (h, s2): the register order of the P / dS packs written in phase 1.
-  auto phase2 = [&](const uint16_t* Qs, const uint16_t* Ds) {
-#pragma unroll 1
-    for (int h = 0; h < 2; ++h) {
-      const int f = __builtin_amdgcn_readfirstlane(Xf[kw + 4 * h]);
-      if (f == 0) continue;
-      const int src = (kw + 4 * h) * 2;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 pb = Xp[(src + s2) * 64 + lane];
-        const bf16x8 db = Xd[(src + s2) * 64 + lane];
-#pragma unroll
-        for (int m = 0; m < MH; ++m) {
-          const bf16x8 at = tr_operand_at<D>(Ds, 32 * h + 16 * s2, trh[m][0], trh[m][1]);
-          const bf16x8 aq = tr_operand_at<D>(Qs, 32 * h + 16 * s2, trh[m][0], trh[m][1]);
-          dvacc[m] = mfma32(at, pb, dvacc[m]);
-          dkacc[m] = mfma32(aq, db, dkacc[m]);
-          if (f == 2) {
-            dvacc[m] = mfma32(at, Xpl[(src + s2) * 64 + lane], dvacc[m]);
-            dkacc[m] = mfma32(aq, Xdl[(src + s2) * 64 + lane], dkacc[m]);
-          }
-        }
-      }
+    // The two waves on a SIMD take the two halves in opposite order, so one
+    // feeds the matrix core while the other works on the vector ALUs.
+    if (rh == 0) {
+      gradients();
+      __builtin_amdgcn_sched_barrier(0);
+      softmax();
+    } else {
+      softmax();
+      __builtin_amdgcn_sched_barrier(0);
+      gradients();
     }
-  };
-
-  // Per tile: wait for its loads (the only ones in flight) and barrier (data
-  // visible; every wave done with the previous tile's stage and exchange),
-  // start loading the next tile into the other stage, phase 1, barrier
-  // (exchange written), phase 2.
-  if (ntiles > 0) issue(Q0, O0, M0s, 0);
-  for (int i = 0; i < ntiles; i += 2) {
-    wg_barrier<kWaitAll>();
-    if (i + 1 < ntiles) issue(Q1, O1, M1s, i + 1);
-    phase1(Q0, O0, M0s, i);
-    wg_barrier<kWaitLgkm>();
-    phase2(Q0, O0);
-    if (i + 1 < ntiles) {
-      wg_barrier<kWaitAll>();
-      if (i + 2 < ntiles) issue(Q0, O0, M0s, i + 2);
-      phase1(Q1, O1, M1s, i + 1);
-      wg_barrier<kWaitLgkm>();
-      phase2(Q1, O1);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      own_h[s2] = new_h[s2];
+      own_l[s2] = new_l[s2];
     }
+    own_f = new_f;
+    if (lane == 0) Xf[xo_cur * NW + wave] = new_f;
+    sc = sn;
   }
 
   if (!key_valid) return;
   const size_t obase = (static_cast<size_t>(my_key) * hkv + g) * D;
+  float* const out = rh ? dk : dv;
+  const float sc_out = rh ? scale : 1.f;
 #pragma unroll
-  for (int m = 0; m < MH; ++m)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      const size_t off = obase + (rh * MH + m) * 32 + 8 * gq + 4 * hi;
-      float4* pk = reinterpret_cast<float4*>(dk + off);
-      float4* pv = reinterpret_cast<float4*>(dv + off);
-      float4 a = *pk, c = *pv;
-      a.x += scale * dkacc[m][4 * gq + 0];
-      a.y += scale * dkacc[m][4 * gq + 1];
-      a.z += scale * dkacc[m][4 * gq + 2];
-      a.w += scale * dkacc[m][4 * gq + 3];
-      c.x += dvacc[m][4 * gq + 0];
-      c.y += dvacc[m][4 * gq + 1];
-      c.z += dvacc[m][4 * gq + 2];
-      c.w += dvacc[m][4 * gq + 3];
-      *pk = a;
-      *pv = c;
+      float4* po = reinterpret_cast<float4*>(out + obase + mb * 32 + 8 * gq + 4 * hi);
+      float4 a = *po;
+      a.x += sc_out * acc[mb][4 * gq + 0];
+      a.y += sc_out * acc[mb][4 * gq + 1];
+      a.z += sc_out * acc[mb][4 * gq + 2];
+      a.w += sc_out * acc[mb][4 * gq + 3];
+      *po = a;
     }
 }
 

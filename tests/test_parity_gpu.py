@@ -44,6 +44,13 @@ SMALL = {
                               branch_len=3, seed_base=1500),
     "dflash_d64_f32": specs.small("f32b", (64, 20), hq=4, hkv=2, d=64, dtype="f32",
                                   branch="dflash", branch_len=8, anchor_stride=8, seed_base=1600),
+    # Long rows with scores of std 0.25: about 95% of the 32x32 (row, key)
+    # blocks of the dK/dV kernel have every P below 2^-8, so they take the
+    # path without the hi+lo split of P and dS (the short cases above almost
+    # always split).
+    "eagle3_long_rows_bf16": specs.small("long", (2600, 300), hq=4, hkv=1, d=128, dtype="bf16",
+                                         branch="eagle3", branch_len=2, value_scale=0.5,
+                                         seed_base=1700),
 }
 
 
