@@ -237,12 +237,13 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
 //     full head dimension.  The partner's half of P (or dS) arrives through
 //     LDS as packed bf16 MFMA operands.
 //
-// Software pipeline (one iteration per tile i, two barriers): the S / dP
-// MFMAs of tile i go to the matrix core before the exchange barrier; after
-// it, the dV / dK MFMAs of tile i-1 run while the same wave computes the
-// softmax gradient of tile i on the vector ALUs.  Q / dO tiles arrive by
-// direct global->LDS loads into a three-stage ring (tile i+1 loading, i in
-// the S / dP step, i-1 in the dV / dK step).
+// One iteration per tile i, two barriers: after the first, the dV / dK MFMAs
+// of tile i-1 (reading the partner packs from LDS) and the S / dP MFMAs of
+// tile i; after the second, the softmax gradient of tile i, which writes the
+// new packs.  All reads of the exchange come before the second barrier and
+// all writes after it, so one exchange buffer suffices.  Q / dO tiles arrive
+// by direct global->LDS loads into a three-stage ring (tile i+1 loading,
+// i in the S / dP step, i-1 in the dV / dK step).
 //
 // Query tiles are visited from the END of the visible range backwards: every
 // key block of a sequence sees the same trailing rows, so the workgroups that
@@ -310,10 +311,9 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
   // meta = lse | delta | seq | pos of its 64 rows
   __shared__ __attribute__((aligned(16))) uint16_t R[3][2 * TS];
   __shared__ __attribute__((aligned(16))) uint32_t Mr[3][4 * TR];
-  // partner-bound packs, MFMA B-operand layout: [wave][k-step][lane] x 8 bf16;
-  // hi parts double-buffered by tile parity, lo parts single-buffered
-  __shared__ __attribute__((aligned(16))) bf16x8 Xh[2 * XN], Xl[XN];
-  __shared__ int Xf[2 * NW];    // 0: nothing visible, 1: hi only, 2: hi + lo
+  // partner-bound packs, MFMA B-operand layout: [wave][k-step][lane] x 8 bf16
+  __shared__ __attribute__((aligned(16))) bf16x8 Xh[XN], Xl[XN];
+  __shared__ int Xf[NW];    // 0: nothing visible, 1: hi only, 2: hi + lo
 
   const float scale_log2 = scale * kLog2e;
   const int nblk = (nk + KB - 1) / KB;
@@ -419,17 +419,67 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
     wg_barrier<kWaitAll>();
     if (i + 1 < ntiles) issue(sn, i + 1);
 
-    // partner packs of tile i-1: hi parts are read where they are used (their
-    // buffer is not rewritten before iteration i+1), lo parts now (the single
-    // lo buffer is rewritten after the next barrier)
-    const int xo_prv = (i + 1) & 1, xo_cur = i & 1;
-    int par_f = 0;
-    bf16x8 par_l[2] = {zero8(), zero8()};
+    // dV^T += dO^T P (rh = 0) or dK^T += Q^T dS (rh = 1) over tile i-1's 64
+    // rows.  Rows 32*h + 16*s2 + 8*(j/4) + 4*hi + (j%4) are k-element j of
+    // k-step (h, s2): the register order of the packs.
     if (i >= 1) {
-      par_f = __builtin_amdgcn_readfirstlane(Xf[xo_prv * NW + partner]);
-      if (par_f == 2) {
+      const uint16_t* At = prv + (rh ? 0 : TS);
+      const int par_f = __builtin_amdgcn_readfirstlane(Xf[partner]);
+      if (own_f == 1 && par_f == 1) {
+        // common case, both halves visible and no split: 4*MB MFMAs, own
+        // rows first, transposed operands loaded kPre MFMAs ahead
+        constexpr int kPre = 4;
+        constexpr int NSTEP = 4 * MB;
+        const uint16_t* Aown = At + 32 * rh * D;
+        const uint16_t* Apar = At + 32 * (1 - rh) * D;
+        const bf16x8 pb0 = Xh[(partner * 2 + 0) * 64 + lane];
+        const bf16x8 pb1 = Xh[(partner * 2 + 1) * 64 + lane];
+        auto load = [&](int j) {
+          const int hh = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
+          return tr_operand<D>(hh == 0 ? Aown : Apar, lo_off, 16 * s2, mb);
+        };
+        bf16x8 opnd[kPre];
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) par_l[s2] = Xl[(partner * 2 + s2) * 64 + lane];
+        for (int j = 0; j < kPre; ++j) opnd[j] = load(j);
+#pragma unroll
+        for (int j = 0; j < NSTEP; ++j) {
+          const int hh = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
+          const bf16x8 b = hh == 0 ? own_h[s2] : (s2 == 0 ? pb0 : pb1);
+          acc[mb] = mfma32(opnd[j % kPre], b, acc[mb]);
+          if (j + kPre < NSTEP) opnd[j % kPre] = load(j + kPre);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 + 2 * kPre, 0);
+#pragma unroll
+        for (int j = 0; j < NSTEP - kPre; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
+      } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bool mine = h == rh;
+        const int f = mine ? own_f : par_f;
+        if (f == 0) continue;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int xi = (partner * 2 + s2) * 64 + lane;
+          const bf16x8 bh = mine ? own_h[s2] : Xh[xi];
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const bf16x8 a = tr_operand<D>(At, lo_off, 32 * h + 16 * s2, mb);
+            acc[mb] = mfma32(a, bh, acc[mb]);
+          }
+          if (f == 2) {
+            const bf16x8 bl = mine ? own_l[s2] : Xl[xi];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+              const bf16x8 a = tr_operand<D>(At, lo_off, 32 * h + 16 * s2, mb);
+              acc[mb] = mfma32(a, bl, acc[mb]);
+            }
+          }
+        }
+      }
       }
     }
 
@@ -456,48 +506,37 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
                     wf_seq == wl_seq && rf_pos >= wl_pos;
       }
       if (active) {
+        // 2*KS MFMAs (S then dP), operands loaded kPre steps ahead
+        constexpr int kPre = 4;
+        bf16x8 opnd[kPre];
+        auto load = [&](int j) {
+          return j < KS ? row_operand<D>(cur, lo_off, r0, j) : row_operand<D>(cur + TS, lo_off, r0, j - KS);
+        };
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          sacc = mfma32(row_operand<D>(cur, lo_off, r0, ks), kreg[ks], sacc);
+        for (int j = 0; j < kPre; ++j) opnd[j] = load(j);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          dpacc = mfma32(row_operand<D>(cur + TS, lo_off, r0, ks), vreg[ks], dpacc);
+        for (int j = 0; j < 2 * KS; ++j) {
+          if (j < KS) sacc = mfma32(opnd[j % kPre], kreg[j], sacc);
+          else dpacc = mfma32(opnd[j % kPre], vreg[j - KS], dpacc);
+          if (j + kPre < 2 * KS) opnd[j % kPre] = load(j + kPre);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+#pragma unroll
+        for (int j = 0; j < 2 * KS - kPre; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
       }
     }
 
-    // every wave has read its partner's lo packs
+    // every wave is done reading the exchange
     wg_barrier<kWaitLgkm>();
 
-    // dV^T += dO^T P (rh = 0) or dK^T += Q^T dS (rh = 1) over tile i-1's 64
-    // rows.  Rows 32*h + 16*s2 + 8*(j/4) + 4*hi + (j%4) are k-element j of
-    // k-step (h, s2): the register order of the packs.
-    auto gradients = [&]() {
-      if (i < 1) return;
-      const uint16_t* At = prv + (rh ? 0 : TS);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bool mine = h == rh;
-        const int f = mine ? own_f : par_f;
-        if (f == 0) continue;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const bf16x8 bh = mine ? own_h[s2] : Xh[xo_prv * XN + (partner * 2 + s2) * 64 + lane];
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            const bf16x8 a = tr_operand<D>(At, lo_off, 32 * h + 16 * s2, mb);
-            acc[mb] = mfma32(a, bh, acc[mb]);
-            if (f == 2) acc[mb] = mfma32(a, mine ? own_l[s2] : par_l[s2], acc[mb]);
-          }
-        }
-      }
-    };
-
-    // softmax gradient of tile i: P, dS; own packs into new_*, partner-bound
-    // packs into the exchange
-    bf16x8 new_h[2] = {zero8(), zero8()}, new_l[2] = {zero8(), zero8()};
-    int new_f = 0;
-    auto softmax = [&]() {
-      if (!active) return;
+    // softmax gradient of tile i: P, dS; own packs replace tile i-1's,
+    // partner-bound packs go to the exchange
+    own_f = 0;
+    if (active) {
       float p[16], ds[16];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
@@ -539,15 +578,15 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) big |= p[r] >= kSplitP;
       const bool split = __any(big);
-      new_f = split ? 2 : 1;
+      own_f = split ? 2 : 1;
       // own: P (rh = 0) or dS (rh = 1); partner-bound: the other one
       auto emit = [&](const float (&mine)[16], const float (&theirs)[16]) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const bf16x8 oh = pack8(&mine[8 * s2]);
           const bf16x8 th = pack8(&theirs[8 * s2]);
-          new_h[s2] = oh;
-          Xh[xo_cur * XN + (wave * 2 + s2) * 64 + lane] = th;
+          own_h[s2] = oh;
+          Xh[(wave * 2 + s2) * 64 + lane] = th;
           if (split) {
             float ol[8], tl[8];
 #pragma unroll
@@ -555,33 +594,15 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
               ol[j] = mine[8 * s2 + j] - static_cast<float>(oh[j]);
               tl[j] = theirs[8 * s2 + j] - static_cast<float>(th[j]);
             }
-            new_l[s2] = pack8(ol);
+            own_l[s2] = pack8(ol);
             Xl[(wave * 2 + s2) * 64 + lane] = pack8(tl);
           }
         }
       };
       if (rh) emit(ds, p);
       else emit(p, ds);
-    };
-
-    // The two waves on a SIMD take the two halves in opposite order, so one
-    // feeds the matrix core while the other works on the vector ALUs.
-    if (rh == 0) {
-      gradients();
-      __builtin_amdgcn_sched_barrier(0);
-      softmax();
-    } else {
-      softmax();
-      __builtin_amdgcn_sched_barrier(0);
-      gradients();
     }
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      own_h[s2] = new_h[s2];
-      own_l[s2] = new_l[s2];
-    }
-    own_f = new_f;
-    if (lane == 0) Xf[xo_cur * NW + wave] = new_f;
+    if (lane == 0) Xf[wave] = own_f;
     sc = sn;
   }
 
