@@ -237,13 +237,22 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
 //     full head dimension.  The partner's half of P (or dS) arrives through
 //     LDS as packed bf16 MFMA operands.
 //
-// One iteration per tile i, two barriers: after the first, the dV / dK MFMAs
-// of tile i-1 (reading the partner packs from LDS) and the S / dP MFMAs of
-// tile i; after the second, the softmax gradient of tile i, which writes the
-// new packs.  All reads of the exchange come before the second barrier and
-// all writes after it, so one exchange buffer suffices.  Q / dO tiles arrive
-// by direct global->LDS loads into a three-stage ring (tile i+1 loading,
-// i in the S / dP step, i-1 in the dV / dK step).
+// Two teams of four waves (key groups 0-1 and 2-3), placed so that the two
+// waves sharing a SIMD belong to different teams.  Each tile takes three
+// steps per wave: GRAD (dV / dK MFMAs of the previous tile, partner packs
+// read from LDS), SDP (S / dP MFMAs of the tile) and SOFT (softmax gradient,
+// writes the packs).  Every wave runs the same loop, one iteration per tile:
+//   barrier, GRAD(i-1) + SDP(i), barrier, SOFT(i)
+// but team 1 runs one barrier behind team 0 (an extra barrier at its start,
+// one at team 0's end), so between any two barriers one wave of each SIMD
+// feeds the matrix core while the other works on the vector ALUs.  A team
+// writes its exchange in one window and reads it in the next, so one
+// exchange buffer suffices.  Team 0 alone loads the Q / dO tiles, by direct
+// global->LDS loads into a three-stage ring: tile i+1 is loaded while team 0
+// works on GRAD(i-1) + SDP(i), into the stage of tile i-2 (whose last reader,
+// team 1's GRAD(i-2), finished before that window), and team 0 waits for it
+// before the barrier that opens its next MFMA window, which team 1 passes
+// before it reads the tile.
 //
 // Query tiles are visited from the END of the visible range backwards: every
 // key block of a sequence sees the same trailing rows, so the workgroups that
@@ -276,18 +285,20 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)p));
 }
 
-// Direct global->LDS loads: lane l writes LDS[lds + l*bytes].  Issued as
-// inline assembly so that the compiler does not guard later LDS reads with
-// waits on these loads: the kernel waits for them itself (vmcnt) before the
-// barrier that publishes a ring stage.  `lds` must be wave-uniform.  The
-// s_nop covers the M0 write -> LDS-DMA hazard.
-__device__ __forceinline__ void dma_b128(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(lds) : "memory", "m0");
+// Direct global->LDS loads: lane l reads global address base + voff (base
+// wave-uniform, in scalar registers; voff a per-lane 32-bit byte offset) and
+// writes LDS[lds + l*bytes].  Issued as inline assembly so that the compiler
+// does not guard later LDS reads with waits on these loads: the kernel waits
+// for them itself (vmcnt) before the barrier that publishes a ring stage.
+// `lds` must be wave-uniform.  The s_nop covers the M0 write -> LDS-DMA
+// hazard.
+__device__ __forceinline__ void dma_b128(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
 }
-__device__ __forceinline__ void dma_b32(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(g), "s"(lds) : "memory", "m0");
+__device__ __forceinline__ void dma_b32(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
 }
 
 template <int D, int G>
@@ -322,9 +333,13 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
   const int kblk = L % nblk;             // early keys are seen by the most rows: heavy first
   const int key0 = kblk * KB;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int kw = wave & 3, rh = wave >> 2;   // key group; row half and role (0: dV, 1: dK)
-  const int partner = wave ^ 4;
+  // wave w: team w / 4, key group 2*team + (w / 2) % 2, row half / role w % 2
+  // (0: dV, 1: dK); waves w and w + 4 share a SIMD under the usual
+  // round-robin placement, and belong to different teams
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int team = wave >> 2;
+  const int kw = 2 * team + ((wave >> 1) & 1), rh = wave & 1;
+  const int partner = wave ^ 1;
   const int n = lane & 31, hi = lane >> 5;
   const LaneOffsets<D> lo_off(lane);
 
@@ -337,8 +352,10 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
   const bool wave_valid = wk0 < nk;
   const int wkl = min(nk, wk0 + 32) - 1;
   const bool wave_complete = wk0 + 32 <= nk;
-  const int wf_seq = wave_valid ? k_seq[wk0] : 0, wf_pos = wave_valid ? k_pos[wk0] : 0;
-  const int wl_seq = wave_valid ? k_seq[wkl] : 0, wl_pos = wave_valid ? k_pos[wkl] : 0;
+  const int wf_seq = __builtin_amdgcn_readfirstlane(wave_valid ? k_seq[wk0] : 0);
+  const int wf_pos = __builtin_amdgcn_readfirstlane(wave_valid ? k_pos[wk0] : 0);
+  const int wl_seq = __builtin_amdgcn_readfirstlane(wave_valid ? k_seq[wkl] : 0);
+  const int wl_pos = __builtin_amdgcn_readfirstlane(wave_valid ? k_pos[wkl] : 0);
 
   // K and V rows of the lane's key as MFMA B operands (k-elements 16*ks + 8*hi ..)
   bf16x8 kreg[KS], vreg[KS];
@@ -354,8 +371,10 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
   // query tokens that can see any key of the block; tile i covers tokens
   // [qhi - (i+1)*TPT, qhi - i*TPT) clipped at qlo
   const int klast = min(nk, key0 + KB) - 1;
-  const int qlo = lower_bound_sp(q_seq, q_pos, nq, k_seq[key0], k_pos[key0]);
-  const int qhi = upper_bound_sp(q_seq, q_pos, nq, k_seq[klast], INT_MAX);
+  const int qlo = __builtin_amdgcn_readfirstlane(
+      lower_bound_sp(q_seq, q_pos, nq, k_seq[key0], k_pos[key0]));
+  const int qhi = __builtin_amdgcn_readfirstlane(
+      upper_bound_sp(q_seq, q_pos, nq, k_seq[klast], INT_MAX));
   const int ntiles = qhi > qlo ? (qhi - qlo + TPT - 1) / TPT : 0;
 
   f32x16 acc[MB];   // dV^T (rh = 0) or dK^T (rh = 1): rows = head-dim columns, cols = keys
@@ -370,173 +389,226 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
 
   auto tile_t0 = [&](int i) { return max(qlo, qhi - (i + 1) * TPT); };
 
-  // Loads of tile i into ring stage st.  Lane l of round `it` of wave w fills
-  // 16-byte slot (it*NW + w)*64 + l of the tile, i.e. physical chunk p of row r;
-  // it fetches logical chunk swz(r, p) (the swizzle is an involution).  Rows
-  // past the tile's end re-read its last row; they are masked by index.
+  // Loads of tile i into ring stage st, issued by the four waves of team 0.
+  // Lane l of round `it` of wave w fills 16-byte slot (it*4 + w)*64 + l of
+  // the tile, i.e. physical chunk p of row r; it fetches logical chunk
+  // swz(r, p) (the swizzle is an involution).  Rows past the tile's end (only
+  // in the tile at the start of the range) re-read its last row; they are
+  // masked by index.  Addresses are a wave-uniform 64-bit base for the tile
+  // plus a per-lane 32-bit byte offset relative to the tile's first token.
+  constexpr int LROUNDS = 2 * QROUNDS;
+  uint32_t lane_off[LROUNDS];   // bytes
+#pragma unroll
+  for (int it = 0; it < LROUNDS; ++it) {
+    const int slot = (it * 4 + (wave & 3)) * 64 + lane;
+    const int r = slot / CPR, p = slot % CPR;
+    lane_off[it] = 2u * (((r / G) * hq + g * G + r % G) * D + 8 * swz<D>(r, p));
+  }
+  // meta: row = lane; lse / delta at [head][token], seq / pos at [token].
+  // Recomputed per tile from an opaque copy of the lane id, so that it is not
+  // kept live (and spilled) across the loop.
+  const bool meta_by_head = (wave & 3) < 2;
+  auto meta_off_of = [&]() {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return 4u * (meta_by_head ? (g * G + l % G) * nq + l / G : l / G);
+  };
+  const char* const meta_src = reinterpret_cast<const char*>(
+      (wave & 3) == 0 ? static_cast<const void*>(lse)
+    : (wave & 3) == 1 ? static_cast<const void*>(delta)
+    : (wave & 3) == 2 ? static_cast<const void*>(q_seq)
+                      : static_cast<const void*>(q_pos));
   auto issue = [&](int st, int i) {
     const int t0 = tile_t0(i);
     const int t1 = qhi - i * TPT;
+    const char* qt = reinterpret_cast<const char*>(q) + static_cast<size_t>(t0) * hq * D * 2;
+    const char* ot = reinterpret_cast<const char*>(dout) + static_cast<size_t>(t0) * hq * D * 2;
+    const char* mt = meta_src + static_cast<size_t>(t0) * 4;
+    if (t1 - t0 == TPT) {
+      dma_b32(mt, meta_off_of(), lds_addr(&Mr[st][wave * TR]));
 #pragma unroll
-    for (int it = 0; it < QROUNDS; ++it) {
-      const int slot = (it * NW + wave) * 64 + lane;
-      const int r = slot / CPR, p = slot % CPR;
-      const int c = swz<D>(r, p);
-      const int tok = min(t0 + r / G, t1 - 1);
-      const int head = g * G + r % G;
-      const size_t off = (static_cast<size_t>(tok) * hq + head) * D + 8 * c;
-      const uint32_t base = __builtin_amdgcn_readfirstlane(
-          lds_addr(&R[st][(it * NW + wave) * 64 * 8]));
-      dma_b128(q + off, base);
-      dma_b128(dout + off, base + TS * 2);
-    }
-    if (wave < 4) {
-      const int r = lane;                      // TR == 64 rows, one per lane
-      const int tok = min(t0 + r / G, t1 - 1);
-      const int head = g * G + r % G;
-      const size_t li = static_cast<size_t>(head) * nq + tok;
-      const void* src = wave == 0 ? static_cast<const void*>(lse + li)
-                      : wave == 1 ? static_cast<const void*>(delta + li)
-                      : wave == 2 ? static_cast<const void*>(q_seq + tok)
-                                  : static_cast<const void*>(q_pos + tok);
-      dma_b32(src, __builtin_amdgcn_readfirstlane(lds_addr(&Mr[st][wave * TR])));
+      for (int it = 0; it < LROUNDS; ++it) {
+        const uint32_t base = lds_addr(&R[st][(it * 4 + wave) * 64 * 8]);
+        dma_b128(qt, lane_off[it], base);
+        dma_b128(ot, lane_off[it], base + TS * 2);
+      }
+    } else {
+      // tile at the start of the range: token index clipped to t1 - 1
+      const int dtok = min(lane / G, t1 - 1 - t0) - lane / G;
+      dma_b32(mt, meta_off_of() + 4 * dtok, lds_addr(&Mr[st][wave * TR]));
+#pragma unroll
+      for (int it = 0; it < LROUNDS; ++it) {
+        const int slot = (it * 4 + wave) * 64 + lane;
+        const int r = slot / CPR;
+        const int dt = min(r / G, t1 - 1 - t0) - r / G;
+        const uint32_t base = lds_addr(&R[st][(it * 4 + wave) * 64 * 8]);
+        const uint32_t off = lane_off[it] + static_cast<uint32_t>(dt * hq * D * 2);
+        dma_b128(qt, off, base);
+        dma_b128(ot, off, base + TS * 2);
+      }
     }
   };
 
-  // Iteration i: S / dP of tile i (stage sc), dV / dK of tile i-1 (stage sp),
-  // loads of tile i+1 into stage sn.  Iterations run 0 .. ntiles; the last
-  // one only finishes tile ntiles-1.
-  if (ntiles > 0) issue(0, 0);
-  int sc = 0;
-  for (int i = 0; i <= ntiles; ++i) {
-    const int sn = sc == 2 ? 0 : sc + 1;
-    const int sp = sc == 0 ? 2 : sc - 1;
-    const uint16_t* const cur = R[sc];
-    const uint16_t* const prv = R[sp];
-    const uint32_t* const M = Mr[sc];
-
-    // tile i landed; X and Xf hold tile i-1's partner packs; stage sn is free
-    wg_barrier<kWaitAll>();
-    if (i + 1 < ntiles) issue(sn, i + 1);
-
-    // dV^T += dO^T P (rh = 0) or dK^T += Q^T dS (rh = 1) over tile i-1's 64
-    // rows.  Rows 32*h + 16*s2 + 8*(j/4) + 4*hi + (j%4) are k-element j of
-    // k-step (h, s2): the register order of the packs.
-    if (i >= 1) {
-      const uint16_t* At = prv + (rh ? 0 : TS);
-      const int par_f = __builtin_amdgcn_readfirstlane(Xf[partner]);
-      if (own_f == 1 && par_f == 1) {
-        // common case, both halves visible and no split: 4*MB MFMAs, own
-        // rows first, transposed operands loaded kPre MFMAs ahead
-        constexpr int kPre = 4;
-        constexpr int NSTEP = 4 * MB;
-        const uint16_t* Aown = At + 32 * rh * D;
-        const uint16_t* Apar = At + 32 * (1 - rh) * D;
-        const bf16x8 pb0 = Xh[(partner * 2 + 0) * 64 + lane];
-        const bf16x8 pb1 = Xh[(partner * 2 + 1) * 64 + lane];
-        auto load = [&](int j) {
-          const int hh = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
-          return tr_operand<D>(hh == 0 ? Aown : Apar, lo_off, 16 * s2, mb);
-        };
-        bf16x8 opnd[kPre];
+  // ---- GRAD: dV^T += dO^T P (rh = 0) or dK^T += Q^T dS (rh = 1) over the
+  // 64 rows of the previous tile, held in ring stage `st`.  Rows
+  // 32*h + 16*s2 + 8*(j/4) + 4*hi + (j%4) are k-element j of k-step (h, s2):
+  // the register order of the packs.
+  auto grad = [&](const uint16_t* tile) {
+    const uint16_t* At = tile + (rh ? 0 : TS);
+    const int par_f = __builtin_amdgcn_readfirstlane(Xf[partner]);
+    if (own_f == 1 && par_f == 1) {
+      // common case, both halves visible and no split: 4*MB MFMAs, own
+      // rows first, transposed operands loaded kPre MFMAs ahead
+      constexpr int kPre = 4;
+      constexpr int NSTEP = 4 * MB;
+      const uint16_t* Aown = At + 32 * rh * D;
+      const uint16_t* Apar = At + 32 * (1 - rh) * D;
+      const bf16x8 pb0 = Xh[(partner * 2 + 0) * 64 + lane];
+      const bf16x8 pb1 = Xh[(partner * 2 + 1) * 64 + lane];
+      auto load = [&](int j) {
+        const int hh = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
+        return tr_operand<D>(hh == 0 ? Aown : Apar, lo_off, 16 * s2, mb);
+      };
+      bf16x8 opnd[kPre];
 #pragma unroll
-        for (int j = 0; j < kPre; ++j) opnd[j] = load(j);
+      for (int j = 0; j < kPre; ++j) opnd[j] = load(j);
 #pragma unroll
-        for (int j = 0; j < NSTEP; ++j) {
-          const int hh = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
-          const bf16x8 b = hh == 0 ? own_h[s2] : (s2 == 0 ? pb0 : pb1);
-          acc[mb] = mfma32(opnd[j % kPre], b, acc[mb]);
-          if (j + kPre < NSTEP) opnd[j % kPre] = load(j + kPre);
+      for (int j = 0; j < NSTEP; ++j) {
+        const int hh = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
+        const bf16x8 b = hh == 0 ? own_h[s2] : (s2 == 0 ? pb0 : pb1);
+        acc[mb] = mfma32(opnd[j % kPre], b, acc[mb]);
+        if (j + kPre < NSTEP) opnd[j % kPre] = load(j + kPre);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 + 2 * kPre, 0);
+#pragma unroll
+      for (int j = 0; j < NSTEP - kPre; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
+      return;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bool mine = h == rh;
+      const int f = mine ? own_f : par_f;
+      if (f == 0) continue;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int xi = (partner * 2 + s2) * 64 + lane;
+        const bf16x8 bh = mine ? own_h[s2] : Xh[xi];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const bf16x8 a = tr_operand<D>(At, lo_off, 32 * h + 16 * s2, mb);
+          acc[mb] = mfma32(a, bh, acc[mb]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 + 2 * kPre, 0);
-#pragma unroll
-        for (int j = 0; j < NSTEP - kPre; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
-      } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bool mine = h == rh;
-        const int f = mine ? own_f : par_f;
-        if (f == 0) continue;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int xi = (partner * 2 + s2) * 64 + lane;
-          const bf16x8 bh = mine ? own_h[s2] : Xh[xi];
+        if (f == 2) {
+          const bf16x8 bl = mine ? own_l[s2] : Xl[xi];
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
             const bf16x8 a = tr_operand<D>(At, lo_off, 32 * h + 16 * s2, mb);
-            acc[mb] = mfma32(a, bh, acc[mb]);
-          }
-          if (f == 2) {
-            const bf16x8 bl = mine ? own_l[s2] : Xl[xi];
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-              const bf16x8 a = tr_operand<D>(At, lo_off, 32 * h + 16 * s2, mb);
-              acc[mb] = mfma32(a, bl, acc[mb]);
-            }
+            acc[mb] = mfma32(a, bl, acc[mb]);
           }
         }
       }
-      }
     }
+  };
 
-    // S = Q K^T, dP = dO V^T of tile i: lane (n = key, hi) register r holds
-    // row r0 + acc_row(r, hi)
-    const float* lse_s = reinterpret_cast<const float*>(M);
-    const float* dl_s = reinterpret_cast<const float*>(M + TR);
-    const int* rseq_s = reinterpret_cast<const int*>(M + 2 * TR);
-    const int* rpos_s = reinterpret_cast<const int*>(M + 3 * TR);
-    const int r0 = 32 * rh;
-    bool active = false, wave_full = false;
-    int nrows = 0;
-    f32x16 sacc = zero16(), dpacc = zero16();
-    if (i < ntiles) {
-      const int t0 = tile_t0(i);
-      nrows = (qhi - i * TPT - t0) * G;
-      if (r0 < nrows) {
-        const int rl = min(nrows, r0 + 32) - 1;
-        const int rf_seq = rseq_s[r0], rf_pos = rpos_s[r0];
-        const int rl_seq = rseq_s[rl], rl_pos = rpos_s[rl];
-        active = wave_valid && !lex_less(rl_seq, rl_pos, wf_seq, wf_pos) &&
-                 !lex_less(wl_seq, INT_MAX, rf_seq, rf_pos);
-        wave_full = wave_complete && rl == r0 + 31 && rf_seq == rl_seq && rf_seq == wf_seq &&
-                    wf_seq == wl_seq && rf_pos >= wl_pos;
-      }
-      if (active) {
-        // 2*KS MFMAs (S then dP), operands loaded kPre steps ahead
-        constexpr int kPre = 4;
-        bf16x8 opnd[kPre];
-        auto load = [&](int j) {
-          return j < KS ? row_operand<D>(cur, lo_off, r0, j) : row_operand<D>(cur + TS, lo_off, r0, j - KS);
-        };
-#pragma unroll
-        for (int j = 0; j < kPre; ++j) opnd[j] = load(j);
-#pragma unroll
-        for (int j = 0; j < 2 * KS; ++j) {
-          if (j < KS) sacc = mfma32(opnd[j % kPre], kreg[j], sacc);
-          else dpacc = mfma32(opnd[j % kPre], vreg[j - KS], dpacc);
-          if (j + kPre < 2 * KS) opnd[j % kPre] = load(j + kPre);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
-#pragma unroll
-        for (int j = 0; j < 2 * KS - kPre; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
-      }
+  // ---- SDP: S = Q K^T, dP = dO V^T of tile i (ring stage st): lane (n = key,
+  // hi) register r holds row r0 + acc_row(r, hi).  The state below carries
+  // the tile to its SOFT step.
+  const int r0 = 32 * rh;
+  bool active = false, wave_full = false;
+  int nrows = 0, soft_st = 0;
+  f32x16 sacc = zero16(), dpacc = zero16();
+  // Visibility of tile i for this wave's key group and row half, from the
+  // sequence / position of the row half's first and last rows in the tile's
+  // meta: LDS reads issued right after the barrier that publishes the tile
+  // (vis_load) and evaluated after the dV / dK MFMAs (vis_eval), so that
+  // their latency stays hidden.
+  bool nx_active = false, nx_full = false;
+  int nx_nrows = 0;
+  int v_nr = 0, v_rl = 0, v_fs = 0, v_fp = 0, v_ls = 0, v_lp = 0;
+  bool v_some = false;
+  auto vis_load = [&](int i, int st) {
+    v_some = false;
+    v_nr = 0;
+    if (i >= ntiles) return;
+    const int t0 = tile_t0(i);
+    v_nr = (qhi - i * TPT - t0) * G;
+    if (r0 >= v_nr) return;
+    v_some = true;
+    v_rl = min(v_nr, r0 + 32) - 1;
+    const int* rseq_s = reinterpret_cast<const int*>(&Mr[st][2 * TR]);
+    const int* rpos_s = reinterpret_cast<const int*>(&Mr[st][3 * TR]);
+    v_fs = rseq_s[r0];
+    v_fp = rpos_s[r0];
+    v_ls = rseq_s[v_rl];
+    v_lp = rpos_s[v_rl];
+  };
+  auto vis_eval = [&]() {
+    nx_nrows = v_nr;
+    nx_active = __builtin_amdgcn_readfirstlane(
+        v_some && wave_valid && !lex_less(v_ls, v_lp, wf_seq, wf_pos) &&
+        !lex_less(wl_seq, INT_MAX, v_fs, v_fp));
+    nx_full = __builtin_amdgcn_readfirstlane(
+        v_some && wave_complete && v_rl == r0 + 31 && v_fs == v_ls && v_fs == wf_seq &&
+        wf_seq == wl_seq && v_fp >= wl_pos);
+  };
+
+  auto sdp = [&](int i, int st) {
+    active = nx_active;
+    wave_full = nx_full;
+    nrows = nx_nrows;
+    soft_st = st;
+    if (i >= ntiles) {
+      sacc = zero16();
+      dpacc = zero16();
+      return;
     }
+    // 2*KS MFMAs (S then dP), operands loaded kPre steps ahead; computed for
+    // every wave so that the accumulators are redefined on every path (rows
+    // past the tile's end hold copies of its last row), used only if active
+    // S and dP MFMAs alternate (j even: S k-step j/2, j odd: dP), so that
+    // consecutive MFMAs are independent and the two accumulation chains
+    // cover each other's result latency
+    const uint16_t* cur = R[st];
+    constexpr int kPre = 8;
+    bf16x8 opnd[kPre];
+    auto load = [&](int j) {
+      return row_operand<D>(cur + (j & 1) * TS, lo_off, r0, j >> 1);
+    };
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) opnd[j] = load(j);
+#pragma unroll
+    for (int j = 0; j < 2 * KS; ++j) {
+      const int ks = j >> 1;
+      if (j == 0) sacc = mfma32(opnd[0], kreg[0], zero16());
+      else if (j == 1) dpacc = mfma32(opnd[1], vreg[0], zero16());
+      else if ((j & 1) == 0) sacc = mfma32(opnd[j % kPre], kreg[ks], sacc);
+      else dpacc = mfma32(opnd[j % kPre], vreg[ks], dpacc);
+      if (j + kPre < 2 * KS) opnd[j % kPre] = load(j + kPre);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+#pragma unroll
+    for (int j = 0; j < 2 * KS - kPre; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
+  };
 
-    // every wave is done reading the exchange
-    wg_barrier<kWaitLgkm>();
-
-    // softmax gradient of tile i: P, dS; own packs replace tile i-1's,
-    // partner-bound packs go to the exchange
+  // ---- SOFT: softmax gradient of the tile last passed to SDP: P, dS; own
+  // packs replace the previous tile's (already used by GRAD), partner-bound
+  // packs go to the exchange.
+  auto soft = [&]() {
     own_f = 0;
     if (active) {
+      const uint32_t* M = Mr[soft_st];
+      const float* lse_s = reinterpret_cast<const float*>(M);
+      const float* dl_s = reinterpret_cast<const float*>(M + TR);
+      const int* rseq_s = reinterpret_cast<const int*>(M + 2 * TR);
+      const int* rpos_s = reinterpret_cast<const int*>(M + 3 * TR);
       float p[16], ds[16];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
@@ -603,8 +675,30 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
       else emit(p, ds);
     }
     if (lane == 0) Xf[wave] = own_f;
+  };
+
+  // Iterations run 0 .. ntiles; tile i sits in stage i % 3.  The last
+  // iteration only finishes tile ntiles-1.
+  if (team == 0 && ntiles > 0) issue(0, 0);
+  if (team == 1) wg_barrier<kWaitLgkm>();
+  int sc = 0;
+  for (int i = 0; i <= ntiles; ++i) {
+    const int sn = sc == 2 ? 0 : sc + 1;
+    const int sp = sc == 0 ? 2 : sc - 1;
+    // MFMA window: tile i landed (team 0 waited for its loads); stage sn
+    // (tile i-2) is free
+    wg_barrier<kWaitAll>();
+    vis_load(i, sc);
+    if (i >= 1) grad(R[sp]);
+    vis_eval();
+    if (team == 0 && i + 1 < ntiles) issue(sn, i + 1);
+    sdp(i, sc);
+    // VALU window
+    wg_barrier<kWaitLgkm>();
+    soft();
     sc = sn;
   }
+  if (team == 0) wg_barrier<kWaitLgkm>();
 
   if (!key_valid) return;
   const size_t obase = (static_cast<size_t>(my_key) * hkv + g) * D;
