@@ -266,41 +266,6 @@ constexpr int TR = 64;         // query rows per tile (2 halves of 32)
 constexpr float kSplitP = 1.f / 256.f;
 }  // namespace bwdkv
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14])
-constexpr int kWaitAll = 0;
-constexpr int kWaitLgkm = 0xC07F;   // lgkmcnt(0), vmcnt and expcnt not waited on
-
-template <int kWait>
-__device__ __forceinline__ void wg_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(kWait);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// 32-bit LDS address of a pointer into __shared__ memory.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)p));
-}
-
-// Direct global->LDS loads: lane l reads global address base + voff (base
-// wave-uniform, in scalar registers; voff a per-lane 32-bit byte offset) and
-// writes LDS[lds + l*bytes].  Issued as inline assembly so that the compiler
-// does not guard later LDS reads with waits on these loads: the kernel waits
-// for them itself (vmcnt) before the barrier that publishes a ring stage.
-// `lds` must be wave-uniform.  The s_nop covers the M0 write -> LDS-DMA
-// hazard.
-__device__ __forceinline__ void dma_b128(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
-}
-__device__ __forceinline__ void dma_b32(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
-}
-
 template <int D, int G>
 __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ q_seq,

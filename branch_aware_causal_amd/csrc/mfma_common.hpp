@@ -144,4 +144,82 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
   return xcd < rem ? xcd * (full + 1) + idx : rem * (full + 1) + (xcd - rem) * full + idx;
 }
 
+// m = max(m, x[0..15]) as eight chained v_max3_f32.  fmaxf would first
+// quiet each operand (IEEE mode), one extra instruction per element, and
+// separate asm statements would each be followed by a hazard nop; the
+// values fed here are finite or -inf.
+__device__ __forceinline__ float max16_raw(float m, const f32x16& x) {
+  asm("v_max3_f32 %0, %0, %1, %2\n\t"
+      "v_max3_f32 %0, %0, %3, %4\n\t"
+      "v_max3_f32 %0, %0, %5, %6\n\t"
+      "v_max3_f32 %0, %0, %7, %8\n\t"
+      "v_max3_f32 %0, %0, %9, %10\n\t"
+      "v_max3_f32 %0, %0, %11, %12\n\t"
+      "v_max3_f32 %0, %0, %13, %14\n\t"
+      "v_max3_f32 %0, %0, %15, %16"
+      : "+v"(m)
+      : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]),
+        "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]), "v"(x[14]),
+        "v"(x[15]));
+  return m;
+}
+
+// max(v, v of lane l ^ 32) without going through LDS.
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Marks v as computed at this point.  Barriers order memory accesses only,
+// so without this the compiler may sink register arithmetic past them.
+__device__ __forceinline__ void keep(float v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void keep(bf16x8 v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void keep(f32x16 v) { asm volatile("" ::"v"(v)); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14])
+constexpr int kWaitAll = 0;
+constexpr int kWaitLgkm = 0xC07F;   // lgkmcnt(0), vmcnt and expcnt not waited on
+constexpr int kWaitNone = 0xCF7F;   // nothing waited on
+
+template <int kWait>
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWait);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 32-bit LDS address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)p));
+}
+
+// Scalar-register copy of a wave-uniform pointer.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Direct global->LDS loads: lane l reads global address base + voff (base
+// wave-uniform, in scalar registers; voff a per-lane 32-bit byte offset) and
+// writes LDS[lds + l*bytes].  Issued as inline assembly so that the compiler
+// does not guard later LDS reads with waits on these loads: the kernel waits
+// for them itself (vmcnt) before the barrier that publishes a ring stage.
+// `lds` must be wave-uniform.  The s_nop covers the M0 write -> LDS-DMA
+// hazard.
+__device__ __forceinline__ void dma_b128(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(uniform_ptr(base)), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(uniform_ptr(base)), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
 }  // namespace bac

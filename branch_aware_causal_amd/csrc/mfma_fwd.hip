@@ -11,10 +11,15 @@
 //     of one kv-head group: 256 (token, q-head) rows that all read the same
 //     K/V tiles.  Wave w owns 32 rows: tokens tok0 + w*32/G + n/G, heads
 //     g*G + n%G for n = 0..31 (the GQA heads of a token are adjacent rows).
-//   * Keys stream through LDS in row-major tiles of 64, double buffered, one
-//     barrier per tile.  The key range of a workgroup is [first key of its
-//     first row's sequence, last key visible to its last row], found by binary
-//     search on the (seq, pos)-sorted shard.
+//   * Keys stream through LDS in row-major tiles of 64, double buffered,
+//     copied straight from global memory into LDS (no register staging).  The
+//     key range of a workgroup is [first key of its first row's sequence, last
+//     key visible to its last row], found by binary search on the (seq,
+//     pos)-sorted shard.  Within it the keys a row sees form one index
+//     interval, also found by binary search, so masks are index compares.
+//   * Ping-pong: waves w and w+4 share a SIMD and run one half-step apart
+//     (barrier between half-steps), so that while one issues the tile's 32
+//     MFMAs the other runs its softmax on the vector ALUs.
 //   * Scores are computed transposed, S^T = K Q^T (keys x rows), so each lane
 //     holds 32 scores of ONE query row: the row max is in-lane plus one
 //     exchange with lane n+32, and the row sums stay per lane until the end.
@@ -36,6 +41,10 @@
 namespace bac {
 
 namespace fwd {
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
 constexpr int BN = 64;          // keys per tile
 constexpr int NW = 8;           // waves per workgroup
 constexpr float kRescale = 8.f; // lazy-rescale threshold (log2 units)
@@ -54,12 +63,9 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
   constexpr int KS = D / 16;            // k-steps of QK^T
   constexpr int MB = D / 32;            // 32-row blocks of O^T
   constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int LOADS = BN * CPR / 512; // 16-byte chunks per thread per tile
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * D];
-  __shared__ __attribute__((aligned(16))) int kseq_s[2][BN];
-  __shared__ __attribute__((aligned(16))) int kpos_s[2][BN];
 
   const int nblk_tok = (nq + TPB - 1) / TPB;
   const int L = xcd_remap(blockIdx.x, nblk_tok * hkv);
@@ -83,8 +89,6 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
   const int wlast = min(nq, wtok0 + TPW) - 1;
   const bool wave_valid = wtok0 < nq;
   const bool wave_complete = wtok0 + TPW <= nq;
-  const int wf_seq = wave_valid ? q_seq[wtok0] : 0, wf_pos = wave_valid ? q_pos[wtok0] : 0;
-  const int wl_seq = wave_valid ? q_seq[wlast] : 0, wl_pos = wave_valid ? q_pos[wlast] : 0;
 
   // ---- key range of the workgroup ----------------------------------------
   const int blast = min(nq, tok0 + TPB) - 1;
@@ -107,139 +111,217 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
   float m_run = kNegInf;   // reference max (log2 units), same in lanes n and n+32
   float l_run = 0.f;       // this lane's part of the running sum
 
-  // ---- tile staging: global -> registers -> LDS ---------------------------
-  uint4 kreg[LOADS], vreg[LOADS];
-  int sreg = 0, preg = 0;
-  auto load_tile = [&](int j0) {
+  // ---- tile loads: direct global -> LDS, issued by team 0 --------------
+  // Lane l of round `it` of team-0 wave w fills 16-byte slot (it*4 + w)*64 + l
+  // of a K (V) tile, i.e. physical chunk p of key row r; it fetches logical
+  // chunk swz(r, p) (the swizzle is an involution).  Keys past the end re-read
+  // the last key; they and keys past hi_k are masked by index.  Addresses are
+  // a wave-uniform base plus a per-lane 32-bit byte offset from the tile's
+  // first key.
+  constexpr int ROUNDS = BN * CPR / 256;
+  uint32_t lane_row[ROUNDS], lane_col[ROUNDS];
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int c = tid + 512 * it;
-      const int key = c / CPR, col = (c % CPR) * 8;
-      const int j = j0 + key;
-      if (j < nk) {
-        const size_t off = (static_cast<size_t>(j) * hkv + g) * D + col;
-        kreg[it] = *reinterpret_cast<const uint4*>(k + off);
-        vreg[it] = *reinterpret_cast<const uint4*>(v + off);
-      } else {
-        kreg[it] = make_uint4(0, 0, 0, 0);
-        vreg[it] = make_uint4(0, 0, 0, 0);
-      }
-    }
-    if (tid < BN) {
-      const int j = j0 + tid;
-      const bool ok = j < hi_k;
-      sreg = ok ? k_seq[j] : INT_MIN;
-      preg = ok ? k_pos[j] : INT_MAX;
-    }
-  };
-  auto store_tile = [&](int b) {
-#pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int c = tid + 512 * it;
-      const int key = c / CPR, col = (c % CPR) * 8;
-      *reinterpret_cast<uint4*>(&Ks[b][toff<D>(key, col)]) = kreg[it];
-      *reinterpret_cast<uint4*>(&Vs[b][toff<D>(key, col)]) = vreg[it];
-    }
-    if (tid < BN) {
-      kseq_s[b][tid] = sreg;
-      kpos_s[b][tid] = preg;
-    }
-  };
-
-  if (ntiles > 0) {
-    load_tile(lo);
-    store_tile(0);
+  for (int it = 0; it < ROUNDS; ++it) {
+    const int slot = (it * 4 + (wave & 3)) * 64 + lane;
+    const int r = slot / CPR, pc = slot % CPR;
+    lane_row[it] = r;
+    lane_col[it] = 2u * (g * D + 8 * swz<D>(r, pc));
   }
-  __syncthreads();
+  const uint32_t krow_bytes = static_cast<uint32_t>(hkv * D * 2);
+  auto issue_rows = [&](const uint16_t* src, uint16_t* dst_tile, int j0) {
+    const char* base = reinterpret_cast<const char*>(src) + static_cast<size_t>(j0) * krow_bytes;
+    const int rmax = nk - 1 - j0;     // last valid key row of the tile
+#pragma unroll
+    for (int it = 0; it < ROUNDS; ++it) {
+      const uint32_t off =
+          static_cast<uint32_t>(min(static_cast<int>(lane_row[it]), rmax)) * krow_bytes + lane_col[it];
+      dma_b128(base, off, lds_addr(dst_tile) + (it * 4 + (wave & 3)) * 64 * 16);
+    }
+  };
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int b = t & 1;
-    const int j0 = lo + t * BN;
-    if (t + 1 < ntiles) load_tile(j0 + BN);
+  // ---- visible keys of each row ------------------------------------------
+  // The shard is sorted by (seq, pos), so the keys a row sees (same sequence,
+  // pos <= its pos) are one index interval [r_lo, r_hi) of [lo, hi_k).  Rows
+  // past nq see nothing.  A wave classifies a tile from the extremes of its
+  // rows' intervals: some row may see it, or every row sees all of it.
+  int r_lo = 0, r_hi = 0;
+  if (row_valid) {
+    r_lo = lo + lower_bound_sp(k_seq + lo, k_pos + lo, hi_k - lo, my_seq, INT_MIN);
+    r_hi = lo + upper_bound_sp(k_seq + lo, k_pos + lo, hi_k - lo, my_seq, my_pos);
+  }
+  int lo_min = row_valid ? r_lo : INT_MAX, hi_max = row_valid ? r_hi : INT_MIN;
+  int lo_max = row_valid ? r_lo : INT_MIN, hi_min = row_valid ? r_hi : INT_MAX;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    lo_min = min(lo_min, __shfl_xor(lo_min, o));
+    hi_max = max(hi_max, __shfl_xor(hi_max, o));
+    lo_max = max(lo_max, __shfl_xor(lo_max, o));
+    hi_min = min(hi_min, __shfl_xor(hi_min, o));
+  }
+  lo_min = __builtin_amdgcn_readfirstlane(lo_min);
+  hi_max = __builtin_amdgcn_readfirstlane(hi_max);
+  lo_max = __builtin_amdgcn_readfirstlane(lo_max);
+  hi_min = __builtin_amdgcn_readfirstlane(hi_min);
+  auto tile_any = [&](int j0) { return lo_min < min(j0 + BN, hi_k) && hi_max > j0; };
+  auto tile_full = [&](int j0) { return wave_complete && lo_max <= j0 && j0 + BN <= hi_min; };
 
-    // classify the tile for this wave
-    const int jl = min(hi_k, j0 + BN) - 1 - j0;      // last in-range key of the tile
-    const int kf_seq = kseq_s[b][0], kf_pos = kpos_s[b][0];
-    const int kl_seq = kseq_s[b][jl], kl_pos = kpos_s[b][jl];
-    const bool wave_any = wave_valid && !lex_less(wl_seq, wl_pos, kf_seq, kf_pos) &&
-                          !lex_less(kl_seq, kl_pos, wf_seq, INT_MIN);
-    const bool wave_full = wave_complete && jl == BN - 1 && kf_seq == kl_seq &&
-                           kf_seq == wf_seq && wf_seq == wl_seq && kl_pos <= wf_pos;
+  // ---- ping-pong schedule ------------------------------------------------
+  // Waves w and w+4 share a SIMD.  Team 0 (waves 0-3) and team 1 (waves 4-7)
+  // run the same sequence of half-steps, team 1 one half-step behind, with a
+  // workgroup barrier between half-steps, so that on every SIMD one wave
+  // feeds the matrix core while the other runs the softmax:
+  //   half-step 2t   : team 0 MFMA(t) = PV(t-1), S(t)   team 1 softmax(t-1)
+  //   half-step 2t+1 : team 0 softmax(t)                 team 1 MFMA(t)
+  // K(t) is read in half-steps 2t and 2t+1, V(t) in 2t+2 and 2t+3.  Team 0
+  // issues K(t+1) and V(t) at the start of half-step 2t and waits for them
+  // before the barrier that ends half-step 2t+1, so both are double buffered.
+  const int team = wave >> 2;
+  if (team == 0 && ntiles > 0) issue_rows(k, &Ks[0][0], lo);
+  wg_barrier<kWaitAll>();
+  if (team == 1) wg_barrier<kWaitNone>();
 
-    if (wave_any) {
-      // S^T = K Q^T over two 32-key blocks: lane (n, hi) register r of block kb
-      // holds key kb*32 + acc_row(r, hi) of query row n.
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          sacc[kb] = mfma32(row_operand<D>(Ks[b], lo_off, kb * 32, ks), qreg[ks], sacc[kb]);
+  f32x16 sacc[2] = {zero16(), zero16()};
+  bf16x8 pb[4] = {zero8(), zero8(), zero8(), zero8()};
+
+  // One MFMA half-step as a single stream: O^T += V^T P^T for tile t-1
+  // (4*MB MFMAs, transposed V operands), then S^T = K Q^T for tile t (2*KS
+  // MFMAs, the two 32-key blocks interleaved).  LDS operands are read kPre
+  // MFMAs ahead.
+  constexpr int kPre = 4;
+  auto mfma_stream = [&](auto pv_c, auto s_c, const uint16_t* vt, const uint16_t* kt) {
+    constexpr bool kPV = decltype(pv_c)::value, kS = decltype(s_c)::value;
+    constexpr int NP = kPV ? 4 * MB : 0, N = NP + (kS ? 2 * KS : 0);
+    auto load = [&](int j) {
+      if (j < NP) {
+        const int kb = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
+        return tr_operand<D>(vt, lo_off, kb * 32 + 16 * s2, mb);
       }
-      // raw scores; masked entries become -inf (scale > 0 keeps the max in place)
-      float x[2][16];
+      const int kb = (j - NP) % 2, ks = (j - NP) / 2;
+      return row_operand<D>(kt, lo_off, kb * 32, ks);
+    };
+    bf16x8 opnd[kPre];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int j = 0; j < kPre; ++j) opnd[j] = load(j);
+    if (kS) {
+      sacc[0] = zero16();
+      sacc[1] = zero16();
+    }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[kb][r] = sacc[kb][r];
-      if (!wave_full) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int t0 = kb * 32 + 8 * r4 + 4 * hi;
-            const int4 ss = *reinterpret_cast<const int4*>(&kseq_s[b][t0]);
-            const int4 pp = *reinterpret_cast<const int4*>(&kpos_s[b][t0]);
-            const int sv[4] = {ss.x, ss.y, ss.z, ss.w};
-            const int pv[4] = {pp.x, pp.y, pp.z, pp.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const bool vis = row_valid & (sv[e] == my_seq) & (pv[e] <= my_pos);
-              x[kb][4 * r4 + e] = vis ? x[kb][4 * r4 + e] : kNegInf;
-            }
-          }
+    for (int j = 0; j < N; ++j) {
+      if (j < NP) {
+        const int kb = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
+        oacc[mb] = mfma32(opnd[j % kPre], pb[2 * kb + s2], oacc[mb]);
+      } else {
+        const int kb = (j - NP) % 2, ks = (j - NP) / 2;
+        sacc[kb] = mfma32(opnd[j % kPre], qreg[ks], sacc[kb]);
       }
-      float mt = kNegInf;
+      if (j + kPre < N) opnd[j % kPre] = load(j + kPre);
+    }
+    // pin the order: kPre operands, then one MFMA and the next operand
+    // (a transposed operand is two LDS reads, a row operand one)
+    static_assert(NP == 0 || NP >= kPre, "prefetch covers one operand kind");
+    if constexpr (NP > 0)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre, 0);
+    else
+      __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int j = 0; j < N; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (j + kPre < NP)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else if (j + kPre < N)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    // the stream stays in its half-step
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(x[kb][r], x[kb][r + 1]));
-      mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
-      // lazy rescale: move the reference only when the tile max clears it by kRescale
-      if (__any(mt > m_run + kRescale)) {
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = (m_run == kNegInf) ? 0.f : exp2_fast(m_run - m_new);
-        l_run *= alpha;
+    for (int mb = 0; mb < MB; ++mb) keep(oacc[mb]);
+    keep(sacc[0]);
+    keep(sacc[1]);
+  };
+
+  // softmax half-step of the tile at j0: scores -> P (bf16) in pb; a tile
+  // this wave skips leaves zeros, so the next MFMA half-step may run its PV
+  // regardless
+  auto softmax = [&](int j0, bool do_s) {
+    if (!do_s) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+      for (int i = 0; i < 4; ++i) pb[i] = zero8();
+      return;
+    }
+    // masked entries become -inf (scale > 0 keeps the max in place); the
+    // softmax works in place on the score registers
+    if (!tile_full(j0)) {
+      const int a = r_lo - j0 - 4 * hi, e_end = r_hi - j0 - 4 * hi;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          x[kb][r] = exp2_fast(fmaf(x[kb][r], scale_log2, -m_use));
-          l_run += x[kb][r];
-        }
-      // O^T += V^T P^T, four k-steps of 16 keys
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const bf16x8 pb = pack8(&x[kb][8 * s2]);
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            oacc[mb] = mfma32(tr_operand<D>(Vs[b], lo_off, kb * 32 + 16 * s2, mb), pb, oacc[mb]);
+          const int c = kb * 32 + 8 * (r / 4) + (r % 4);
+          sacc[kb][r] = (c >= a && c < e_end) ? sacc[kb][r] : kNegInf;
         }
     }
+    float mt = max16_raw(max16_raw(kNegInf, sacc[0]), sacc[1]);
+    mt = max_xor32(mt) * scale_log2;
+    // lazy rescale: move the reference only when the tile max clears it by kRescale
+    if (__any(mt > m_run + kRescale)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = (m_run == kNegInf) ? 0.f : exp2_fast(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = exp2_fast(fmaf(sacc[kb][r], scale_log2, -m_use));
+        l_run += p[r];
+      }
+      pb[2 * kb] = pack8(&p[0]);
+      pb[2 * kb + 1] = pack8(&p[8]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) keep(pb[i]);
+    keep(l_run);
+  };
 
-    if (t + 1 < ntiles) store_tile(b ^ 1);
-    __syncthreads();
+  // t = 0: S(0) only
+  bool any_prev = false;
+  if (ntiles > 0) {
+    if (team == 0) {
+      if (ntiles > 1) issue_rows(k, &Ks[1][0], lo + BN);
+      issue_rows(v, &Vs[0][0], lo);
+    }
+    const bool do_s = tile_any(lo);
+    if (do_s) mfma_stream(BoolC<false>(), BoolC<true>(), &Vs[1][0], &Ks[0][0]);
+    wg_barrier<kWaitNone>();
+    softmax(lo, do_s);
+    any_prev = do_s;
+    wg_barrier<kWaitAll>();     // team 0's loads of this tile pair have landed
   }
+  // 0 < t < ntiles: PV(t-1) and S(t) as one stream
+  for (int t = 1; t < ntiles; ++t) {
+    const int j0 = lo + t * BN;
+    if (team == 0) {
+      if (t + 1 < ntiles) issue_rows(k, &Ks[(t + 1) & 1][0], j0 + BN);
+      issue_rows(v, &Vs[t & 1][0], j0);
+    }
+    const bool do_s = tile_any(j0);
+    if (any_prev || do_s) mfma_stream(BoolC<true>(), BoolC<true>(), &Vs[(t - 1) & 1][0], &Ks[t & 1][0]);
+    wg_barrier<kWaitNone>();
+    softmax(j0, do_s);
+    any_prev = do_s;
+    wg_barrier<kWaitAll>();
+  }
+  // t = ntiles: PV(ntiles-1) only
+  if (any_prev) mfma_stream(BoolC<true>(), BoolC<false>(), &Vs[(ntiles - 1) & 1][0], &Ks[0][0]);
+  wg_barrier<kWaitNone>();
+  if (team == 0) wg_barrier<kWaitNone>();
 
   // ---- epilogue: normalise, merge, store ---------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
