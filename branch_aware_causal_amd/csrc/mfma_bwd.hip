@@ -30,6 +30,25 @@ constexpr int BN = 64;
 constexpr int NW = 8;
 }  // namespace bwdq
 
+// dq kernel layout:
+//   * A workgroup has 8 waves and owns TPB = 8 * 32/G consecutive query
+//     tokens of one kv-head group; wave w owns 32 (token, head) rows, one per
+//     lane pair (n, n+32).  Q stays in registers, the wave's dO rows in LDS.
+//   * Keys stream through LDS in tiles of 64, copied straight from global
+//     memory (K in a ring of three, V in a ring of two).  The keys a row sees
+//     are one index interval of the (seq, pos)-sorted shard, found by binary
+//     search, so masks are index compares.
+//   * Ping-pong: waves w and w+4 share a SIMD; team 0 (waves 0-3) and team 1
+//     (waves 4-7) run the same half-steps one apart with a barrier between
+//     half-steps:
+//       half-step 2t   : team 0 MFMA(t)             team 1 GRAD(t-1)
+//       half-step 2t+1 : team 0 GRAD(t)             team 1 MFMA(t)
+//     MFMA(t) = dQ^T += K^T dS^T for tile t-1, then S^T = K Q^T and
+//     dP^T = V dO^T for tile t, as one stream of 48 MFMAs with LDS operands
+//     read ahead; GRAD(t) = dS = P (dP - Delta) on the vector ALUs.  K(t) is
+//     read in half-steps 2t .. 2t+3, V(t) in 2t and 2t+1.  Team 0 loads
+//     K(t+1) and V(t+1) at the start of half-step 2t and waits for them
+//     before the barrier that ends half-step 2t+1.
 template <int D, int G>
 __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ q_seq,
@@ -44,12 +63,9 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
   constexpr int KS = D / 16;
   constexpr int MB = D / 32;
   constexpr int CPR = D / 8;
-  constexpr int LOADS = BN * CPR / 512;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * D];   // keys x d, swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[3][BN * D];   // keys x d, swizzled
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * D];
-  __shared__ __attribute__((aligned(16))) int kseq_s[2][BN];
-  __shared__ __attribute__((aligned(16))) int kpos_s[2][BN];
   __shared__ __attribute__((aligned(16))) uint16_t dOs[NW][32 * D];  // each wave's dO rows
 
   const float scale_log2 = scale * kLog2e;
@@ -59,7 +75,7 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
   const int tb = nblk_tok - 1 - (L % nblk_tok);
   const int tok0 = tb * TPB;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int n = lane & 31, hi = lane >> 5;
   const LaneOffsets<D> lo_off(lane);
 
@@ -72,14 +88,9 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
   const size_t li = static_cast<size_t>(my_head) * nq + my_tok;
   const float my_lse2 = row_valid ? lse[li] * kLog2e : kNegInf;
   const float my_delta = row_valid ? delta[li] : 0.f;
-  const bool row_live = row_valid && my_lse2 != kNegInf;
-  const float lse_use = row_live ? my_lse2 : 0.f;
-
-  const int wlast = min(nq, wtok0 + TPW) - 1;
-  const bool wave_valid = wtok0 < nq;
+  // a row with lse = -inf sees no key anywhere, so it is masked everywhere
+  const float lse_use = my_lse2 != kNegInf ? my_lse2 : 0.f;
   const bool wave_complete = wtok0 + TPW <= nq;
-  const int wf_seq = wave_valid ? q_seq[wtok0] : 0, wf_pos = wave_valid ? q_pos[wtok0] : 0;
-  const int wl_seq = wave_valid ? q_seq[wlast] : 0, wl_pos = wave_valid ? q_pos[wlast] : 0;
 
   const int blast = min(nq, tok0 + TPB) - 1;
   const int lo = lower_bound_sp(k_seq, k_pos, nk, q_seq[tok0], INT_MIN);
@@ -103,111 +114,215 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) dqacc[mb] = zero16();
 
-  uint4 kreg[LOADS], vreg[LOADS];
-  int sreg = 0, preg = 0;
-  auto load_tile = [&](int j0) {
+  // ---- tile loads: direct global -> LDS by team 0 -------------------------
+  // Lane l of round `it` of team-0 wave w fills 16-byte slot (it*4 + w)*64 + l
+  // of a tile, i.e. physical chunk p of key row r; it fetches logical chunk
+  // swz(r, p) (the swizzle is an involution).  Keys past the end re-read the
+  // last key; they and keys past hi_k are masked by index.
+  constexpr int ROUNDS = BN * CPR / 256;
+  uint32_t lane_row[ROUNDS], lane_col[ROUNDS];
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int c = tid + 512 * it;
-      const int key = c / CPR, col = (c % CPR) * 8;
-      const int j = j0 + key;
-      if (j < nk) {
-        const size_t off = (static_cast<size_t>(j) * hkv + g) * D + col;
-        kreg[it] = *reinterpret_cast<const uint4*>(k + off);
-        vreg[it] = *reinterpret_cast<const uint4*>(v + off);
-      } else {
-        kreg[it] = make_uint4(0, 0, 0, 0);
-        vreg[it] = make_uint4(0, 0, 0, 0);
-      }
-    }
-    if (tid < BN) {
-      const int j = j0 + tid;
-      const bool ok = j < hi_k;
-      sreg = ok ? k_seq[j] : INT_MIN;
-      preg = ok ? k_pos[j] : INT_MAX;
-    }
-  };
-  auto store_tile = [&](int b) {
-#pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int c = tid + 512 * it;
-      const int key = c / CPR, col = (c % CPR) * 8;
-      *reinterpret_cast<uint4*>(&Ks[b][toff<D>(key, col)]) = kreg[it];
-      *reinterpret_cast<uint4*>(&Vs[b][toff<D>(key, col)]) = vreg[it];
-    }
-    if (tid < BN) {
-      kseq_s[b][tid] = sreg;
-      kpos_s[b][tid] = preg;
-    }
-  };
-
-  if (ntiles > 0) {
-    load_tile(lo);
-    store_tile(0);
+  for (int it = 0; it < ROUNDS; ++it) {
+    const int slot = (it * 4 + (wave & 3)) * 64 + lane;
+    const int r = slot / CPR, pc = slot % CPR;
+    lane_row[it] = r;
+    lane_col[it] = 2u * (g * D + 8 * swz<D>(r, pc));
   }
-  __syncthreads();
+  const uint32_t krow_bytes = static_cast<uint32_t>(hkv * D * 2);
+  auto issue_rows = [&](const uint16_t* src, const uint16_t* dst_tile, int j0) {
+    const char* base = reinterpret_cast<const char*>(src) + static_cast<size_t>(j0) * krow_bytes;
+    const int rmax = nk - 1 - j0;     // last valid key row of the tile
+#pragma unroll
+    for (int it = 0; it < ROUNDS; ++it) {
+      const uint32_t off =
+          static_cast<uint32_t>(min(static_cast<int>(lane_row[it]), rmax)) * krow_bytes + lane_col[it];
+      dma_b128(base, off, lds_addr(dst_tile) + (it * 4 + (wave & 3)) * 64 * 16);
+    }
+  };
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int b = t & 1;
-    const int j0 = lo + t * BN;
-    if (t + 1 < ntiles) load_tile(j0 + BN);
+  // ---- visible keys of each row (see the forward kernel) -----------------
+  int r_lo = 0, r_hi = 0;
+  if (row_valid) {
+    r_lo = lo + lower_bound_sp(k_seq + lo, k_pos + lo, hi_k - lo, my_seq, INT_MIN);
+    r_hi = lo + upper_bound_sp(k_seq + lo, k_pos + lo, hi_k - lo, my_seq, my_pos);
+  }
+  int lo_min = row_valid ? r_lo : INT_MAX, hi_max = row_valid ? r_hi : INT_MIN;
+  int lo_max = row_valid ? r_lo : INT_MIN, hi_min = row_valid ? r_hi : INT_MAX;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    lo_min = min(lo_min, __shfl_xor(lo_min, o));
+    hi_max = max(hi_max, __shfl_xor(hi_max, o));
+    lo_max = max(lo_max, __shfl_xor(lo_max, o));
+    hi_min = min(hi_min, __shfl_xor(hi_min, o));
+  }
+  lo_min = __builtin_amdgcn_readfirstlane(lo_min);
+  hi_max = __builtin_amdgcn_readfirstlane(hi_max);
+  lo_max = __builtin_amdgcn_readfirstlane(lo_max);
+  hi_min = __builtin_amdgcn_readfirstlane(hi_min);
+  auto tile_any = [&](int j0) { return lo_min < min(j0 + BN, hi_k) && hi_max > j0; };
+  auto tile_full = [&](int j0) { return wave_complete && lo_max <= j0 && j0 + BN <= hi_min; };
 
-    const int jl = min(hi_k, j0 + BN) - 1 - j0;
-    const int kf_seq = kseq_s[b][0], kf_pos = kpos_s[b][0];
-    const int kl_seq = kseq_s[b][jl], kl_pos = kpos_s[b][jl];
-    const bool wave_any = wave_valid && !lex_less(wl_seq, wl_pos, kf_seq, kf_pos) &&
-                          !lex_less(kl_seq, kl_pos, wf_seq, INT_MIN);
-    const bool wave_full = wave_complete && jl == BN - 1 && kf_seq == kl_seq &&
-                           kf_seq == wf_seq && wf_seq == wl_seq && kl_pos <= wf_pos;
+  const int team = wave >> 2;
+  if (team == 0 && ntiles > 0) {
+    issue_rows(k, &Ks[0][0], lo);
+    issue_rows(v, &Vs[0][0], lo);
+  }
+  wg_barrier<kWaitAll>();     // also publishes the dO rows
+  if (team == 1) wg_barrier<kWaitNone>();
 
-    if (wave_any) {
+  f32x16 sacc[2] = {zero16(), zero16()}, dpacc[2] = {zero16(), zero16()};
+  bf16x8 db[4] = {zero8(), zero8(), zero8(), zero8()};
+
+  // One MFMA half-step as a single stream: dQ^T += K^T dS^T for the previous
+  // tile (4*MB MFMAs, transposed K operands), then S^T = K Q^T and
+  // dP^T = V dO^T for this tile (4*KS MFMAs, alternating).  LDS operands are
+  // read kPre MFMAs ahead.
+  constexpr int kPre = 4;
+  auto mfma_stream = [&](auto dq_c, auto s_c, const uint16_t* kprev, const uint16_t* kt,
+                         const uint16_t* vt) {
+    constexpr bool kDQ = decltype(dq_c)::value, kS = decltype(s_c)::value;
+    constexpr int NP = kDQ ? 4 * MB : 0, N = NP + (kS ? 4 * KS : 0);
+    // step j >= NP: i = j - NP; S (even i) / dP (odd i) of block kb, k-step ks
+    auto load_a = [&](int j) {
+      if (j < NP) {
+        const int kb = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
+        return tr_operand<D>(kprev, lo_off, kb * 32 + 16 * s2, mb);
+      }
+      const int i = j - NP, kb = (i / 2) % 2, ks = i / 4;
+      return row_operand<D>((i & 1) ? vt : kt, lo_off, kb * 32, ks);
+    };
+    auto load_b = [&](int j) {   // dO operand of a dP step
+      const int ks = (j - NP) / 4;
+      return row_operand<D>(my_do, lo_off, 0, ks);
+    };
+    auto is_dp = [&](int j) { return j >= NP && ((j - NP) & 1); };
+    bf16x8 opa[kPre], opb[kPre];
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+      opa[j] = load_a(j);
+      if (is_dp(j)) opb[j] = load_b(j);
+    }
+    if (kS) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        // S^T = K Q^T and dP^T = V dO^T: lane (n, hi) register r holds key
-        // kb*32 + acc_row(r, hi) of query row n
-        f32x16 sacc = zero16(), dpacc = zero16();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          sacc = mfma32(row_operand<D>(Ks[b], lo_off, kb * 32, ks), qreg[ks], sacc);
-          dpacc = mfma32(row_operand<D>(Vs[b], lo_off, kb * 32, ks),
-                         row_operand<D>(my_do, lo_off, 0, ks), dpacc);
-        }
-        float ds[16];
-        if (wave_full) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            ds[r] = exp2_fast(fmaf(sacc[r], scale_log2, -lse_use)) * (dpacc[r] - my_delta);
-        } else {
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int t0 = kb * 32 + 8 * r4 + 4 * hi;
-            const int4 ss = *reinterpret_cast<const int4*>(&kseq_s[b][t0]);
-            const int4 pp = *reinterpret_cast<const int4*>(&kpos_s[b][t0]);
-            const int sv[4] = {ss.x, ss.y, ss.z, ss.w};
-            const int pv[4] = {pp.x, pp.y, pp.z, pp.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * r4 + e;
-              const bool vis = row_live & (sv[e] == my_seq) & (pv[e] <= my_pos);
-              const float p = exp2_fast(fmaf(sacc[r], scale_log2, -lse_use));
-              ds[r] = vis ? p * (dpacc[r] - my_delta) : 0.f;
-            }
-          }
-        }
-        // dQ^T += K^T dS^T over the 32 keys of this block (2 k-steps)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const bf16x8 db = pack8(&ds[8 * s2]);
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            dqacc[mb] = mfma32(tr_operand<D>(Ks[b], lo_off, kb * 32 + 16 * s2, mb), db, dqacc[mb]);
-        }
+        sacc[kb] = zero16();
+        dpacc[kb] = zero16();
       }
     }
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      if (j < NP) {
+        const int kb = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
+        dqacc[mb] = mfma32(opa[j % kPre], db[2 * kb + s2], dqacc[mb]);
+      } else {
+        const int i = j - NP, kb = (i / 2) % 2, ks = i / 4;
+        if (i & 1)
+          dpacc[kb] = mfma32(opa[j % kPre], opb[j % kPre], dpacc[kb]);
+        else
+          sacc[kb] = mfma32(opa[j % kPre], qreg[ks], sacc[kb]);
+      }
+      if (j + kPre < N) {
+        opa[j % kPre] = load_a(j + kPre);
+        if (is_dp(j + kPre)) opb[j % kPre] = load_b(j + kPre);
+      }
+    }
+    // pin the order: the first kPre steps' operands, then one MFMA and the
+    // operands of the step kPre ahead (2 LDS reads for dQ and dP steps, 1 for S)
+    static_assert(NP == 0 || NP >= kPre, "prefetch covers one operand kind");
+    static_assert(kPre % 2 == 0, "S / dP alternate");
+    if constexpr (NP > 0)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre, 0);
+    else
+      __builtin_amdgcn_sched_group_barrier(0x100, 3 * kPre / 2, 0);
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (j + kPre < NP || (j + kPre < N && is_dp(j + kPre)))
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else if (j + kPre < N)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    // the stream stays in its half-step
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) keep(dqacc[mb]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      keep(sacc[kb]);
+      keep(dpacc[kb]);
+    }
+  };
 
-    if (t + 1 < ntiles) store_tile(b ^ 1);
-    __syncthreads();
+  // GRAD half-step of the tile at j0: dS (bf16) into db; a tile this wave
+  // skips leaves zeros, so the next MFMA half-step may run its dQ regardless
+  auto grad = [&](int j0, bool do_s) {
+    if (!do_s) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) db[i] = zero8();
+      return;
+    }
+    const bool full = tile_full(j0);
+    const int a = r_lo - j0 - 4 * hi, e_end = r_hi - j0 - 4 * hi;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_fast(fmaf(sacc[kb][r], scale_log2, -lse_use));
+        ds[r] = p * (dpacc[kb][r] - my_delta);
+      }
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = kb * 32 + 8 * (r / 4) + (r % 4);
+          ds[r] = (c >= a && c < e_end) ? ds[r] : 0.f;
+        }
+      }
+      db[2 * kb] = pack8(&ds[0]);
+      db[2 * kb + 1] = pack8(&ds[8]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) keep(db[i]);
+  };
+
+  // t = 0: S(0), dP(0) only
+  bool any_prev = false;
+  if (ntiles > 0) {
+    if (team == 0) {
+      if (ntiles > 1) {
+        issue_rows(k, &Ks[1][0], lo + BN);
+        issue_rows(v, &Vs[1][0], lo + BN);
+      }
+    }
+    const bool do_s = tile_any(lo);
+    if (do_s) mfma_stream(BoolC<false>(), BoolC<true>(), &Ks[2][0], &Ks[0][0], &Vs[0][0]);
+    wg_barrier<kWaitNone>();
+    grad(lo, do_s);
+    any_prev = do_s;
+    wg_barrier<kWaitAll>();     // team 0's loads of this tile pair have landed
   }
+  // 0 < t < ntiles: dQ(t-1), S(t), dP(t) as one stream; c = t % 3
+  int c = 1;
+  for (int t = 1; t < ntiles; ++t) {
+    const int j0 = lo + t * BN;
+    const int cn = c == 2 ? 0 : c + 1, cp = c == 0 ? 2 : c - 1;
+    if (team == 0 && t + 1 < ntiles) {
+      issue_rows(k, &Ks[cn][0], j0 + BN);
+      issue_rows(v, &Vs[(t + 1) & 1][0], j0 + BN);
+    }
+    const bool do_s = tile_any(j0);
+    if (any_prev || do_s)
+      mfma_stream(BoolC<true>(), BoolC<true>(), &Ks[cp][0], &Ks[c][0], &Vs[t & 1][0]);
+    wg_barrier<kWaitNone>();
+    grad(j0, do_s);
+    any_prev = do_s;
+    wg_barrier<kWaitAll>();
+    c = cn;
+  }
+  // t = ntiles: dQ(ntiles-1) only
+  if (any_prev)
+    mfma_stream(BoolC<true>(), BoolC<false>(), &Ks[(ntiles - 1) % 3][0], &Ks[0][0], &Vs[0][0]);
+  wg_barrier<kWaitNone>();
+  if (team == 0) wg_barrier<kWaitNone>();
 
   if (!row_valid) return;
   const size_t obase = (static_cast<size_t>(my_tok) * hq + my_head) * D;

@@ -176,6 +176,12 @@ __device__ __forceinline__ void keep(float v) { asm volatile("" ::"v"(v)); }
 __device__ __forceinline__ void keep(bf16x8 v) { asm volatile("" ::"v"(v)); }
 __device__ __forceinline__ void keep(f32x16 v) { asm volatile("" ::"v"(v)); }
 
+// Compile-time flag as a value, to pick lambda variants.
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14])

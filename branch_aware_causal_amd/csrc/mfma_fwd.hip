@@ -41,10 +41,6 @@
 namespace bac {
 
 namespace fwd {
-template <bool B>
-struct BoolC {
-  static constexpr bool value = B;
-};
 constexpr int BN = 64;          // keys per tile
 constexpr int NW = 8;           // waves per workgroup
 constexpr float kRescale = 8.f; // lazy-rescale threshold (log2 units)
