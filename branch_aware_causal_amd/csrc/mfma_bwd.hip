@@ -364,10 +364,11 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
 // writes its exchange in one window and reads it in the next, so one
 // exchange buffer suffices.  Team 0 alone loads the Q / dO tiles, by direct
 // global->LDS loads into a three-stage ring: tile i+1 is loaded while team 0
-// works on GRAD(i-1) + SDP(i), into the stage of tile i-2 (whose last reader,
-// team 1's GRAD(i-2), finished before that window), and team 0 waits for it
-// before the barrier that opens its next MFMA window, which team 1 passes
-// before it reads the tile.
+// works on GRAD(i-1) + SDP(i) (its load rounds spread over the SDP MFMAs, so
+// that no burst of them stalls the wave) into the stage of tile i-2, whose
+// last reader, team 1's GRAD(i-2), finished before that window; team 0 waits
+// for it before the barrier that opens its next MFMA window, which team 1
+// passes before it reads the tile.
 //
 // Query tiles are visited from the END of the visible range backwards: every
 // key block of a sequence sees the same trailing rows, so the workgroups that
@@ -498,35 +499,27 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
     : (wave & 3) == 1 ? static_cast<const void*>(delta)
     : (wave & 3) == 2 ? static_cast<const void*>(q_seq)
                       : static_cast<const void*>(q_pos));
-  auto issue = [&](int st, int i) {
+  // One round of the loads of tile i into stage st: 16 bytes of Q and of dO
+  // per lane.  Rows past the tile's end (only in the tile at the start of
+  // the range) re-read its last row; they are masked by index.
+  auto issue_round = [&](int st, int i, int it) {
     const int t0 = tile_t0(i);
     const int t1 = qhi - i * TPT;
     const char* qt = reinterpret_cast<const char*>(q) + static_cast<size_t>(t0) * hq * D * 2;
     const char* ot = reinterpret_cast<const char*>(dout) + static_cast<size_t>(t0) * hq * D * 2;
+    const int r = ((it * 4 + (wave & 3)) * 64 + lane) / CPR;
+    const int dt = min(r / G, t1 - 1 - t0) - r / G;
+    const uint32_t base = lds_addr(&R[st][(it * 4 + (wave & 3)) * 64 * 8]);
+    const uint32_t off = lane_off[it] + static_cast<uint32_t>(dt * hq * D * 2);
+    dma_b128(qt, off, base);
+    dma_b128(ot, off, base + TS * 2);
+  };
+  auto issue_meta = [&](int st, int i) {
+    const int t0 = tile_t0(i);
+    const int t1 = qhi - i * TPT;
     const char* mt = meta_src + static_cast<size_t>(t0) * 4;
-    if (t1 - t0 == TPT) {
-      dma_b32(mt, meta_off_of(), lds_addr(&Mr[st][wave * TR]));
-#pragma unroll
-      for (int it = 0; it < LROUNDS; ++it) {
-        const uint32_t base = lds_addr(&R[st][(it * 4 + wave) * 64 * 8]);
-        dma_b128(qt, lane_off[it], base);
-        dma_b128(ot, lane_off[it], base + TS * 2);
-      }
-    } else {
-      // tile at the start of the range: token index clipped to t1 - 1
-      const int dtok = min(lane / G, t1 - 1 - t0) - lane / G;
-      dma_b32(mt, meta_off_of() + 4 * dtok, lds_addr(&Mr[st][wave * TR]));
-#pragma unroll
-      for (int it = 0; it < LROUNDS; ++it) {
-        const int slot = (it * 4 + wave) * 64 + lane;
-        const int r = slot / CPR;
-        const int dt = min(r / G, t1 - 1 - t0) - r / G;
-        const uint32_t base = lds_addr(&R[st][(it * 4 + wave) * 64 * 8]);
-        const uint32_t off = lane_off[it] + static_cast<uint32_t>(dt * hq * D * 2);
-        dma_b128(qt, off, base);
-        dma_b128(ot, off, base + TS * 2);
-      }
-    }
+    const int dtok = min(lane / G, t1 - 1 - t0) - lane / G;
+    dma_b32(mt, meta_off_of() + 4 * dtok, lds_addr(&Mr[st][(wave & 3) * TR]));
   };
 
   // ---- GRAD: dV^T += dO^T P (rh = 0) or dK^T += Q^T dS (rh = 1) over the
@@ -636,7 +629,9 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
         wf_seq == wl_seq && v_fp >= wl_pos);
   };
 
-  auto sdp = [&](int i, int st) {
+  auto sdp = [&](int i, int st, auto dma_c, int dst, int di) {
+    constexpr bool kDMA = decltype(dma_c)::value;
+    static_assert(2 * LROUNDS + 1 < 2 * KS, "load rounds fit in the stream");
     active = nx_active;
     wave_full = nx_full;
     nrows = nx_nrows;
@@ -644,6 +639,11 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
     if (i >= ntiles) {
       sacc = zero16();
       dpacc = zero16();
+      if (kDMA) {
+#pragma unroll
+        for (int it = 0; it < LROUNDS; ++it) issue_round(dst, di, it);
+        issue_meta(dst, di);
+      }
       return;
     }
     // 2*KS MFMAs (S then dP), operands loaded kPre steps ahead; computed for
@@ -651,7 +651,9 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
     // past the tile's end hold copies of its last row), used only if active
     // S and dP MFMAs alternate (j even: S k-step j/2, j odd: dP), so that
     // consecutive MFMAs are independent and the two accumulation chains
-    // cover each other's result latency
+    // cover each other's result latency.  Team 0 spreads the loads of the
+    // next tile over the stream (one round every other MFMA), so that no
+    // burst of them stalls the wave.
     const uint16_t* cur = R[st];
     constexpr int kPre = 8;
     bf16x8 opnd[kPre];
@@ -668,6 +670,8 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
       else if ((j & 1) == 0) sacc = mfma32(opnd[j % kPre], kreg[ks], sacc);
       else dpacc = mfma32(opnd[j % kPre], vreg[ks], dpacc);
       if (j + kPre < 2 * KS) opnd[j % kPre] = load(j + kPre);
+      if (kDMA && (j & 1) && j / 2 < LROUNDS) issue_round(dst, di, j / 2);
+      if (kDMA && j == 2 * LROUNDS + 1) issue_meta(dst, di);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
 #pragma unroll
@@ -726,25 +730,31 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
       // weight would otherwise carry bf16's 2^-9 relative rounding into the
       // key's gradient with a large coefficient.  Below the threshold the
       // dropped lo terms are at most kSplitP * 2^-9 each.
-      bool big = false;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) big |= p[r] >= kSplitP;
-      const bool split = __any(big);
-      own_f = split ? 2 : 1;
-      // own: P (rh = 0) or dS (rh = 1); partner-bound: the other one
+      // own: P (rh = 0) or dS (rh = 1); partner-bound: the other one.  The
+      // partner-bound hi packs are written first, so that their LDS latency
+      // overlaps the rest of the step.
       auto emit = [&](const float (&mine)[16], const float (&theirs)[16]) {
+        bf16x8 th[2];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const bf16x8 oh = pack8(&mine[8 * s2]);
-          const bf16x8 th = pack8(&theirs[8 * s2]);
-          own_h[s2] = oh;
-          Xh[(wave * 2 + s2) * 64 + lane] = th;
-          if (split) {
+          th[s2] = pack8(&theirs[8 * s2]);
+          Xh[(wave * 2 + s2) * 64 + lane] = th[s2];
+        }
+        f32x16 pv;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pv[r] = p[r];
+        const bool split = __any(max16_raw(0.f, pv) >= kSplitP);
+        own_f = split ? 2 : 1;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) own_h[s2] = pack8(&mine[8 * s2]);
+        if (split) {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
             float ol[8], tl[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-              ol[j] = mine[8 * s2 + j] - static_cast<float>(oh[j]);
-              tl[j] = theirs[8 * s2 + j] - static_cast<float>(th[j]);
+              ol[j] = mine[8 * s2 + j] - static_cast<float>(own_h[s2][j]);
+              tl[j] = theirs[8 * s2 + j] - static_cast<float>(th[s2][j]);
             }
             own_l[s2] = pack8(ol);
             Xl[(wave * 2 + s2) * 64 + lane] = pack8(tl);
@@ -759,7 +769,11 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
 
   // Iterations run 0 .. ntiles; tile i sits in stage i % 3.  The last
   // iteration only finishes tile ntiles-1.
-  if (team == 0 && ntiles > 0) issue(0, 0);
+  if (team == 0 && ntiles > 0) {
+#pragma unroll
+    for (int it = 0; it < LROUNDS; ++it) issue_round(0, 0, it);
+    issue_meta(0, 0);
+  }
   if (team == 1) wg_barrier<kWaitLgkm>();
   int sc = 0;
   for (int i = 0; i <= ntiles; ++i) {
@@ -771,8 +785,10 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
     vis_load(i, sc);
     if (i >= 1) grad(R[sp]);
     vis_eval();
-    if (team == 0 && i + 1 < ntiles) issue(sn, i + 1);
-    sdp(i, sc);
+    if (team == 0 && i + 1 < ntiles)
+      sdp(i, sc, BoolC<true>(), sn, i + 1);
+    else
+      sdp(i, sc, BoolC<false>(), 0, 0);
     // VALU window
     wg_barrier<kWaitLgkm>();
     soft();
