@@ -49,9 +49,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# headers the MFMA kernel sources include (a change in any of them changes the kernels)
+KERNEL_HEADERS = ["branch_aware_causal_amd/csrc/mfma_common.hpp",
+                  "branch_aware_causal_amd/csrc/device_common.hpp",
+                  "branch_aware_causal_amd/csrc/launch.hpp"]
+
+
 def source_sha(rel):
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for p in [rel] + KERNEL_HEADERS:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 class Timer:
