@@ -124,15 +124,17 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
     lane_col[it] = 2u * (g * D + 8 * swz<D>(r, pc));
   }
   const uint32_t krow_bytes = static_cast<uint32_t>(hkv * D * 2);
-  auto issue_rows = [&](const uint16_t* src, uint16_t* dst_tile, int j0) {
+  // round `it` of the load of the tile at j0 from src into the LDS tile dst
+  auto issue_round = [&](const uint16_t* src, const uint16_t* dst_tile, int j0, int it) {
     const char* base = reinterpret_cast<const char*>(src) + static_cast<size_t>(j0) * krow_bytes;
     const int rmax = nk - 1 - j0;     // last valid key row of the tile
+    const uint32_t off =
+        static_cast<uint32_t>(min(static_cast<int>(lane_row[it]), rmax)) * krow_bytes + lane_col[it];
+    dma_b128(base, off, lds_addr(dst_tile) + (it * 4 + (wave & 3)) * 64 * 16);
+  };
+  auto issue_rows = [&](const uint16_t* src, const uint16_t* dst_tile, int j0) {
 #pragma unroll
-    for (int it = 0; it < ROUNDS; ++it) {
-      const uint32_t off =
-          static_cast<uint32_t>(min(static_cast<int>(lane_row[it]), rmax)) * krow_bytes + lane_col[it];
-      dma_b128(base, off, lds_addr(dst_tile) + (it * 4 + (wave & 3)) * 64 * 16);
-    }
+    for (int it = 0; it < ROUNDS; ++it) issue_round(src, dst_tile, j0, it);
   };
 
   // ---- visible keys of each row ------------------------------------------
@@ -184,9 +186,16 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
   // MFMAs, the two 32-key blocks interleaved).  LDS operands are read kPre
   // MFMAs ahead.
   constexpr int kPre = 4;
-  auto mfma_stream = [&](auto pv_c, auto s_c, const uint16_t* vt, const uint16_t* kt) {
+  // With loads (team 0), the rounds of K(kj0) -> kdst and V(vj0) -> vdst are
+  // spread over the stream, one every N / (2*ROUNDS) MFMAs, so that no burst
+  // of them stalls the wave.
+  auto mfma_stream = [&](auto pv_c, auto s_c, auto dma_c, const uint16_t* vt, const uint16_t* kt,
+                         const uint16_t* kdst, int kj0, const uint16_t* vdst, int vj0) {
     constexpr bool kPV = decltype(pv_c)::value, kS = decltype(s_c)::value;
+    constexpr bool kDMA = decltype(dma_c)::value;
     constexpr int NP = kPV ? 4 * MB : 0, N = NP + (kS ? 2 * KS : 0);
+    constexpr int kGap = N / (2 * ROUNDS);
+    static_assert(!kDMA || kGap >= 1, "load rounds fit in the stream");
     auto load = [&](int j) {
       if (j < NP) {
         const int kb = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
@@ -212,6 +221,13 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
         sacc[kb] = mfma32(opnd[j % kPre], qreg[ks], sacc[kb]);
       }
       if (j + kPre < N) opnd[j % kPre] = load(j + kPre);
+      if (kDMA && j % kGap == 0 && j / kGap < 2 * ROUNDS) {
+        const int r = j / kGap;
+        if (r & 1)
+          issue_round(v, vdst, vj0, r / 2);
+        else
+          issue_round(k, kdst, kj0, r / 2);
+      }
     }
     // pin the order: kPre operands, then one MFMA and the next operand
     // (a transposed operand is two LDS reads, a row operand one)
@@ -294,28 +310,44 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
       issue_rows(v, &Vs[0][0], lo);
     }
     const bool do_s = tile_any(lo);
-    if (do_s) mfma_stream(BoolC<false>(), BoolC<true>(), &Vs[1][0], &Ks[0][0]);
+    if (do_s)
+      mfma_stream(BoolC<false>(), BoolC<true>(), BoolC<false>(), &Vs[1][0], &Ks[0][0], nullptr, 0, nullptr,
+                  0);
     wg_barrier<kWaitNone>();
     softmax(lo, do_s);
     any_prev = do_s;
     wg_barrier<kWaitAll>();     // team 0's loads of this tile pair have landed
   }
   // 0 < t < ntiles: PV(t-1) and S(t) as one stream
+  // team 0 loads K(t+1) and V(t); past the last tile K repeats the last tile
+  // into the buffer of K(t-1), which no later half-step reads
   for (int t = 1; t < ntiles; ++t) {
     const int j0 = lo + t * BN;
-    if (team == 0) {
-      if (t + 1 < ntiles) issue_rows(k, &Ks[(t + 1) & 1][0], j0 + BN);
-      issue_rows(v, &Vs[t & 1][0], j0);
-    }
+    const int kj0 = min(j0 + BN, lo + (ntiles - 1) * BN);
+    const uint16_t* kdst = &Ks[(t + 1) & 1][0];
+    const uint16_t* vdst = &Vs[t & 1][0];
     const bool do_s = tile_any(j0);
-    if (any_prev || do_s) mfma_stream(BoolC<true>(), BoolC<true>(), &Vs[(t - 1) & 1][0], &Ks[t & 1][0]);
+    const uint16_t* vt = &Vs[(t - 1) & 1][0];
+    const uint16_t* kt = &Ks[t & 1][0];
+    if (team == 0) {
+      if (any_prev || do_s) {
+        mfma_stream(BoolC<true>(), BoolC<true>(), BoolC<true>(), vt, kt, kdst, kj0, vdst, j0);
+      } else {
+        issue_rows(k, kdst, kj0);
+        issue_rows(v, vdst, j0);
+      }
+    } else if (any_prev || do_s) {
+      mfma_stream(BoolC<true>(), BoolC<true>(), BoolC<false>(), vt, kt, kdst, kj0, vdst, j0);
+    }
     wg_barrier<kWaitNone>();
     softmax(j0, do_s);
     any_prev = do_s;
     wg_barrier<kWaitAll>();
   }
   // t = ntiles: PV(ntiles-1) only
-  if (any_prev) mfma_stream(BoolC<true>(), BoolC<false>(), &Vs[(ntiles - 1) & 1][0], &Ks[0][0]);
+  if (any_prev)
+    mfma_stream(BoolC<true>(), BoolC<false>(), BoolC<false>(), &Vs[(ntiles - 1) & 1][0], &Ks[0][0], nullptr,
+                0, nullptr, 0);
   wg_barrier<kWaitNone>();
   if (team == 0) wg_barrier<kWaitNone>();
 
