@@ -341,46 +341,60 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV: key-outer.  The workgroup owns 128 keys of one kv-head; the query
-// rows that can see them stream through in tiles of 64 rows.
+// dK / dV: key-outer.  The workgroup owns 128 keys of one kv-head (four key
+// groups of 32); the query rows that can see them stream through in tiles of
+// 32 rows, visited from the END of the visible range backwards (every key
+// block of a sequence sees the same trailing rows, so the workgroups an XCD
+// runs together read the same tiles at nearly the same time, through L2).
 //
-// Eight waves, two per SIMD.  Wave w = (kw, rh) = (w % 4, w / 4):
-//   * for tile rows 32*rh .. +31 and key group kw (32 keys; K and V held in
-//     registers) it computes S, dP, P and dS;
-//   * the wave with rh = 0 accumulates dV^T = dO^T P and the one with rh = 1
-//     dK^T = Q^T dS for the key group, each over the tile's 64 rows and the
-//     full head dimension.  The partner's half of P (or dS) arrives through
-//     LDS as packed bf16 MFMA operands.
+// Eight waves in two teams; waves w and w+4 share a SIMD and serve key
+// group w:
+//   * producer (waves 0-3): K and V of the group's 32 keys in registers as
+//     MFMA A operands; per tile, S^T = K Q^T and dP^T = V dO^T (one query row
+//     per lane), then P = exp2(s*c - lse2) and dS = P (dP - Delta); P and dS
+//     go to LDS as bf16 [row][key] tiles (hi + lo pairs where some P of the
+//     tile reaches kSplitP, see below), with a flag per group;
+//   * consumer (waves 4-7): dV^T += dO^T P and dK^T += Q^T dS for the group
+//     over the tile's rows, both operands by transposing LDS reads, the
+//     accumulators in registers for the whole block.
+// Two barriers per tile.  Half-step 1 of iteration i: the producer runs the
+// S / dP MFMAs of tile i while the consumer reads the P / dS tiles of tile
+// i-1 into registers; half-step 2: the producer's softmax gradient of tile i
+// (vector ALUs) overlaps the consumer's dV / dK MFMAs of tile i-1 on the
+// same SIMD.  Q / dO tiles and their rows' lse, Delta, seq, pos come by
+// direct global->LDS loads, issued by the consumer waves in half-step 1
+// (where they only read the exchange tiles), into a four-stage ring: tile
+// i+2 is loaded in iteration i into the stage of tile i-2 (whose last
+// reader, the consumer's tile i-2, finished in iteration i-1), and each
+// consumer waits for its loads of tile i+1 at the barrier that opens
+// iteration i+1, keeping only its newest batch in flight.  Past the last
+// tile the loads repeat the last tile into a stage no later iteration
+// reads.  The producer reads a tile's row meta before its MFMAs and decides
+// afterwards whether the group sees the tile.
 //
-// Two teams of four waves (key groups 0-1 and 2-3), placed so that the two
-// waves sharing a SIMD belong to different teams.  Each tile takes three
-// steps per wave: GRAD (dV / dK MFMAs of the previous tile, partner packs
-// read from LDS), SDP (S / dP MFMAs of the tile) and SOFT (softmax gradient,
-// writes the packs).  Every wave runs the same loop, one iteration per tile:
-//   barrier, GRAD(i-1) + SDP(i), barrier, SOFT(i)
-// but team 1 runs one barrier behind team 0 (an extra barrier at its start,
-// one at team 0's end), so between any two barriers one wave of each SIMD
-// feeds the matrix core while the other works on the vector ALUs.  A team
-// writes its exchange in one window and reads it in the next, so one
-// exchange buffer suffices.  Team 0 alone loads the Q / dO tiles, by direct
-// global->LDS loads into a three-stage ring: tile i+1 is loaded while team 0
-// works on GRAD(i-1) + SDP(i) (its load rounds spread over the SDP MFMAs, so
-// that no burst of them stalls the wave) into the stage of tile i-2, whose
-// last reader, team 1's GRAD(i-2), finished before that window; team 0 waits
-// for it before the barrier that opens its next MFMA window, which team 1
-// passes before it reads the tile.
-//
-// Query tiles are visited from the END of the visible range backwards: every
-// key block of a sequence sees the same trailing rows, so the workgroups that
-// an XCD runs together read the same tiles at nearly the same time and share
-// them through L2.
+// Exchange-tile columns are keys in the producer's register order: column
+// 16*hi + r holds key 8*(r/4) + 4*hi + (r%4), so a producer lane writes its
+// 16 values of one row as 32 contiguous bytes and the consumer's output
+// column c belongs to key kmap(c).  Rows have a stride of 48 elements, which
+// keeps the transposing reads free of bank conflicts.
 // ---------------------------------------------------------------------------
 namespace bwdkv {
 constexpr int NW = 8;          // waves per workgroup
 constexpr int KB = 128;        // keys per workgroup (4 key groups of 32)
-constexpr int TR = 64;         // query rows per tile (2 halves of 32)
+constexpr int TR = 32;         // query rows per tile
+constexpr int NST = 4;         // ring stages
+constexpr int XS = 48;         // row stride (elements) of an exchange tile
+constexpr int MS = 64;         // stride (entries) of one meta array in a stage
 constexpr float kSplitP = 1.f / 256.f;
+__device__ __forceinline__ int kmap(int c) { return 8 * ((c & 15) >> 2) + 4 * (c >> 4) + (c & 3); }
 }  // namespace bwdkv
+
+// s_waitcnt immediate: vmcnt(n) (n <= 15) and lgkmcnt(0)
+template <int n>
+constexpr int wait_vm_lgkm() {
+  static_assert(n >= 0 && n <= 15, "vmcnt immediate");
+  return 0x0070 | n;
+}
 
 template <int D, int G>
 __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
@@ -391,21 +405,21 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
     const uint16_t* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv) {
   using namespace bwdkv;
-  constexpr int TPT = TR / G;               // tokens per tile
+  constexpr int TPT = TR / G;                  // tokens per tile
   constexpr int KS = D / 16;
   constexpr int MB = D / 32;
   constexpr int CPR = D / 8;
-  constexpr int TS = TR * D;                // elements of one tensor tile
-  constexpr int QROUNDS = TR * CPR / 512;   // 16-byte DMA rounds per thread per tensor per tile
-  constexpr int XN = NW * 2 * 64;           // packs per exchange buffer
+  constexpr int TS = TR * D;                   // elements of one tensor tile
+  constexpr int CROUNDS = 2 * TR * CPR / 256;  // 16-byte load rounds per consumer wave per tile (Q and dO)
+  constexpr int XT = TR * XS;                  // elements of one exchange tile
+  static_assert(TPT >= 1, "at most 32 q-heads per kv-head");
 
-  // three-stage ring; a stage holds Q | dO (rows x d, swizzled) and
-  // meta = lse | delta | seq | pos of its 64 rows
-  __shared__ __attribute__((aligned(16))) uint16_t R[3][2 * TS];
-  __shared__ __attribute__((aligned(16))) uint32_t Mr[3][4 * TR];
-  // partner-bound packs, MFMA B-operand layout: [wave][k-step][lane] x 8 bf16
-  __shared__ __attribute__((aligned(16))) bf16x8 Xh[XN], Xl[XN];
-  __shared__ int Xf[NW];    // 0: nothing visible, 1: hi only, 2: hi + lo
+  __shared__ __attribute__((aligned(16))) uint16_t R[NST][2 * TS];   // Q | dO, rows x d, swizzled
+  __shared__ __attribute__((aligned(16))) uint32_t Mr[NST][4 * MS];  // lse | delta | seq | pos
+  __shared__ __attribute__((aligned(16))) uint16_t X[4][4][XT];     // [group][P, dS, P lo, dS lo]
+  __shared__ __attribute__((aligned(16))) int kseq_s[KB];
+  __shared__ __attribute__((aligned(16))) int kpos_s[KB];
+  __shared__ int Xf[4];   // per group: 0 nothing visible, 1 hi only, 2 hi + lo
 
   const float scale_log2 = scale * kLog2e;
   const int nblk = (nk + KB - 1) / KB;
@@ -414,39 +428,16 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
   const int kblk = L % nblk;             // early keys are seen by the most rows: heavy first
   const int key0 = kblk * KB;
   const int tid = threadIdx.x;
-  // wave w: team w / 4, key group 2*team + (w / 2) % 2, row half / role w % 2
-  // (0: dV, 1: dK); waves w and w + 4 share a SIMD under the usual
-  // round-robin placement, and belong to different teams
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int team = wave >> 2;
-  const int kw = 2 * team + ((wave >> 1) & 1), rh = wave & 1;
-  const int partner = wave ^ 1;
+  const int team = wave >> 2, kg = wave & 3;
   const int n = lane & 31, hi = lane >> 5;
   const LaneOffsets<D> lo_off(lane);
+  const int wk0 = key0 + 32 * kg;        // first key of the group
 
-  // this lane's key (column n of the wave's 32-key group)
-  const int my_key = key0 + kw * 32 + n;
-  const bool key_valid = my_key < nk;
-  const int kseq = key_valid ? k_seq[my_key] : INT_MIN;
-  const int kpos = key_valid ? k_pos[my_key] : INT_MAX;
-  const int wk0 = key0 + kw * 32;
-  const bool wave_valid = wk0 < nk;
-  const int wkl = min(nk, wk0 + 32) - 1;
-  const bool wave_complete = wk0 + 32 <= nk;
-  const int wf_seq = __builtin_amdgcn_readfirstlane(wave_valid ? k_seq[wk0] : 0);
-  const int wf_pos = __builtin_amdgcn_readfirstlane(wave_valid ? k_pos[wk0] : 0);
-  const int wl_seq = __builtin_amdgcn_readfirstlane(wave_valid ? k_seq[wkl] : 0);
-  const int wl_pos = __builtin_amdgcn_readfirstlane(wave_valid ? k_pos[wkl] : 0);
-
-  // K and V rows of the lane's key as MFMA B operands (k-elements 16*ks + 8*hi ..)
-  bf16x8 kreg[KS], vreg[KS];
-  {
-    const size_t kb = (static_cast<size_t>(key_valid ? my_key : 0) * hkv + g) * D + 8 * hi;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kreg[ks] = key_valid ? *reinterpret_cast<const bf16x8*>(k + kb + 16 * ks) : zero8();
-      vreg[ks] = key_valid ? *reinterpret_cast<const bf16x8*>(v + kb + 16 * ks) : zero8();
-    }
+  if (tid < KB) {
+    const bool ok = key0 + tid < nk;
+    kseq_s[tid] = ok ? k_seq[key0 + tid] : INT_MIN;
+    kpos_s[tid] = ok ? k_pos[key0 + tid] : INT_MAX;
   }
 
   // query tokens that can see any key of the block; tile i covers tokens
@@ -457,361 +448,317 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
   const int qhi = __builtin_amdgcn_readfirstlane(
       upper_bound_sp(q_seq, q_pos, nq, k_seq[klast], INT_MAX));
   const int ntiles = qhi > qlo ? (qhi - qlo + TPT - 1) / TPT : 0;
-
-  f32x16 acc[MB];   // dV^T (rh = 0) or dK^T (rh = 1): rows = head-dim columns, cols = keys
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = zero16();
-  // this wave's own packs (P for rh = 0, dS for rh = 1) of the previous tile.
-  // Every pack is defined on every path (zero where unused): the lo MFMAs are
-  // conditional, and undefined operands on the untaken side have let the
-  // compiler produce wrong accumulators.
-  bf16x8 own_h[2] = {zero8(), zero8()}, own_l[2] = {zero8(), zero8()};
-  int own_f = 0;
-
   auto tile_t0 = [&](int i) { return max(qlo, qhi - (i + 1) * TPT); };
 
-  // Loads of tile i into ring stage st, issued by the four waves of team 0.
-  // Lane l of round `it` of wave w fills 16-byte slot (it*4 + w)*64 + l of
-  // the tile, i.e. physical chunk p of row r; it fetches logical chunk
-  // swz(r, p) (the swizzle is an involution).  Rows past the tile's end (only
-  // in the tile at the start of the range) re-read its last row; they are
-  // masked by index.  Addresses are a wave-uniform 64-bit base for the tile
-  // plus a per-lane 32-bit byte offset relative to the tile's first token.
-  constexpr int LROUNDS = 2 * QROUNDS;
-  uint32_t lane_off[LROUNDS];   // bytes
+  // ---- loads of tile i into stage st, by the consumer waves --------------
+  // Lane l of round `it` of consumer wave w (w = wave % 4) fills 16-byte slot
+  // (it*4 + w)*64 + l of the stage (Q then dO), i.e. physical chunk p of row r
+  // of one tensor; it fetches logical chunk swz(r, p) (the swizzle is an
+  // involution).  Rows past the tile's end (only in the tile at the start of
+  // the range) re-read its last row; they are masked by index.  Each consumer
+  // wave also loads one meta array (lse, Delta, seq, pos; lanes 32-63 fill
+  // padding).  CROUNDS + 1 loads per wave and tile.
+  uint32_t lane_off[CROUNDS];   // bytes from the tile's first token, row 0 head 0
+  int lane_tok[CROUNDS];        // token offset of the lane's row
 #pragma unroll
-  for (int it = 0; it < LROUNDS; ++it) {
-    const int slot = (it * 4 + (wave & 3)) * 64 + lane;
-    const int r = slot / CPR, p = slot % CPR;
-    lane_off[it] = 2u * (((r / G) * hq + g * G + r % G) * D + 8 * swz<D>(r, p));
+  for (int it = 0; it < CROUNDS; ++it) {
+    const int slot = (it * 4 + kg) * 64 + lane;
+    const int s2 = slot % (TR * CPR);
+    const int r = s2 / CPR, p = s2 % CPR;
+    lane_tok[it] = r / G;
+    lane_off[it] = 2u * static_cast<uint32_t>(((r / G) * hq + g * G + r % G) * D + 8 * swz<D>(r, p));
   }
-  // meta: row = lane; lse / delta at [head][token], seq / pos at [token].
-  // Recomputed per tile from an opaque copy of the lane id, so that it is not
-  // kept live (and spilled) across the loop.
-  const bool meta_by_head = (wave & 3) < 2;
-  auto meta_off_of = [&]() {
-    int l = lane;
-    asm volatile("" : "+v"(l));
-    return 4u * (meta_by_head ? (g * G + l % G) * nq + l / G : l / G);
-  };
   const char* const meta_src = reinterpret_cast<const char*>(
-      (wave & 3) == 0 ? static_cast<const void*>(lse)
-    : (wave & 3) == 1 ? static_cast<const void*>(delta)
-    : (wave & 3) == 2 ? static_cast<const void*>(q_seq)
-                      : static_cast<const void*>(q_pos));
-  // One round of the loads of tile i into stage st: 16 bytes of Q and of dO
-  // per lane.  Rows past the tile's end (only in the tile at the start of
-  // the range) re-read its last row; they are masked by index.
-  auto issue_round = [&](int st, int i, int it) {
+      kg == 0 ? static_cast<const void*>(lse)
+    : kg == 1 ? static_cast<const void*>(delta)
+    : kg == 2 ? static_cast<const void*>(q_seq)
+              : static_cast<const void*>(q_pos));
+  // load number j (0 .. CROUNDS) of tile i into stage st
+  auto issue_one = [&](int st, int i, int j) {
     const int t0 = tile_t0(i);
-    const int t1 = qhi - i * TPT;
-    const char* qt = reinterpret_cast<const char*>(q) + static_cast<size_t>(t0) * hq * D * 2;
-    const char* ot = reinterpret_cast<const char*>(dout) + static_cast<size_t>(t0) * hq * D * 2;
-    const int r = ((it * 4 + (wave & 3)) * 64 + lane) / CPR;
-    const int dt = min(r / G, t1 - 1 - t0) - r / G;
-    const uint32_t base = lds_addr(&R[st][(it * 4 + (wave & 3)) * 64 * 8]);
-    const uint32_t off = lane_off[it] + static_cast<uint32_t>(dt * hq * D * 2);
-    dma_b128(qt, off, base);
-    dma_b128(ot, off, base + TS * 2);
+    const int tmax = qhi - i * TPT - 1 - t0;   // last token offset of the tile
+    if (j < CROUNDS) {
+      const int tensor = ((j * 4 + kg) * 64) / (TR * CPR);   // wave-uniform
+      const char* src = reinterpret_cast<const char*>(tensor == 0 ? q : dout) +
+                        static_cast<size_t>(t0) * hq * D * 2;
+      const int dt = min(lane_tok[j], tmax) - lane_tok[j];
+      const uint32_t off = lane_off[j] + static_cast<uint32_t>(dt * hq * D * 2);
+      dma_b128(src, off, lds_addr(&R[st][(j * 4 + kg) * 64 * 8]));
+    } else {
+      const int r = min(lane, TR - 1);
+      const int tok = min(r / G, tmax);
+      const uint32_t off = 4u * static_cast<uint32_t>(kg < 2 ? (g * G + r % G) * nq + tok : tok);
+      dma_b32(meta_src + static_cast<size_t>(t0) * 4, off, lds_addr(&Mr[st][kg * MS]));
+    }
   };
-  auto issue_meta = [&](int st, int i) {
-    const int t0 = tile_t0(i);
-    const int t1 = qhi - i * TPT;
-    const char* mt = meta_src + static_cast<size_t>(t0) * 4;
-    const int dtok = min(lane / G, t1 - 1 - t0) - lane / G;
-    dma_b32(mt, meta_off_of() + 4 * dtok, lds_addr(&Mr[st][(wave & 3) * TR]));
+  auto issue = [&](int st, int i) {
+#pragma unroll
+    for (int j = 0; j <= CROUNDS; ++j) issue_one(st, i, j);
   };
 
-  // ---- GRAD: dV^T += dO^T P (rh = 0) or dK^T += Q^T dS (rh = 1) over the
-  // 64 rows of the previous tile, held in ring stage `st`.  Rows
-  // 32*h + 16*s2 + 8*(j/4) + 4*hi + (j%4) are k-element j of k-step (h, s2):
-  // the register order of the packs.
-  auto grad = [&](const uint16_t* tile) {
-    const uint16_t* At = tile + (rh ? 0 : TS);
-    const int par_f = __builtin_amdgcn_readfirstlane(Xf[partner]);
-    if (own_f == 1 && par_f == 1) {
-      // common case, both halves visible and no split: 4*MB MFMAs, own
-      // rows first, transposed operands loaded kPre MFMAs ahead
+  if (ntiles > 0 && team == 1) {
+    issue(0, 0);
+    issue(1, min(1, ntiles - 1));
+  }
+  wg_barrier<kWaitAll>();   // also publishes the key meta
+
+  if (team == 0) {
+    // ======================= producer: S, dP, P, dS =========================
+    const int wkl = min(nk, wk0 + 32) - 1;
+    const bool wave_valid = wk0 < nk;
+    const bool wave_complete = wk0 + 32 <= nk;
+    const int kf_seq = __builtin_amdgcn_readfirstlane(wave_valid ? kseq_s[32 * kg] : 0);
+    const int kf_pos = __builtin_amdgcn_readfirstlane(wave_valid ? kpos_s[32 * kg] : 0);
+    const int kl_seq = __builtin_amdgcn_readfirstlane(wave_valid ? kseq_s[wkl - key0] : 0);
+    const int kl_pos = __builtin_amdgcn_readfirstlane(wave_valid ? kpos_s[wkl - key0] : 0);
+    // K and V rows of the lane's key as MFMA A operands (k-elements 16*ks + 8*hi ..)
+    bf16x8 kreg[KS], vreg[KS];
+    {
+      const bool key_valid = wk0 + n < nk;
+      const size_t kb = (static_cast<size_t>(key_valid ? wk0 + n : 0) * hkv + g) * D + 8 * hi;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        kreg[ks] = key_valid ? *reinterpret_cast<const bf16x8*>(k + kb + 16 * ks) : zero8();
+        vreg[ks] = key_valid ? *reinterpret_cast<const bf16x8*>(v + kb + 16 * ks) : zero8();
+      }
+    }
+    f32x16 sacc = zero16(), dpacc = zero16();
+    for (int i = 0; i <= ntiles; ++i) {
+      // half-step 1: tile i landed (the consumers waited for their loads of it)
+      if (i > 0) wg_barrier<kWaitLgkm>();
+      const int st = i % NST;
+      int nrows = 0, fs = 0, fp = 0, ls = 0, lp = 0;
+      float lse_n = 0.f, dl = 0.f;
+      int rseq = 0, rpos = 0;
+      if (i < ntiles) {
+        // this tile's row meta: read now, used after the MFMAs
+        const int t0 = tile_t0(i);
+        nrows = (qhi - i * TPT - t0) * G;
+        const int* rseq_s = reinterpret_cast<const int*>(&Mr[st][2 * MS]);
+        const int* rpos_s = reinterpret_cast<const int*>(&Mr[st][3 * MS]);
+        fs = rseq_s[0];
+        fp = rpos_s[0];
+        ls = rseq_s[nrows - 1];
+        lp = rpos_s[nrows - 1];
+        lse_n = reinterpret_cast<const float*>(&Mr[st][0])[n];
+        dl = reinterpret_cast<const float*>(&Mr[st][MS])[n];
+        rseq = rseq_s[n];
+        rpos = rpos_s[n];
+        // S^T = K Q^T and dP^T = V dO^T, alternating, B operands (one query
+        // row per lane) loaded kPre MFMAs ahead: lane (n, hi) register r
+        // holds key 8*(r/4) + 4*hi + (r%4) of row n.  Computed for every
+        // tile; used only if the group sees some of its rows.
+        const uint16_t* cur = R[st];
+        constexpr int kPre = 8;
+        bf16x8 opnd[kPre];
+        auto load = [&](int j) { return row_operand<D>(cur + (j & 1) * TS, lo_off, 0, j >> 1); };
+#pragma unroll
+        for (int j = 0; j < kPre; ++j) opnd[j] = load(j);
+#pragma unroll
+        for (int j = 0; j < 2 * KS; ++j) {
+          const int ks = j >> 1;
+          if (j == 0) sacc = mfma32(kreg[0], opnd[0], zero16());
+          else if (j == 1) dpacc = mfma32(vreg[0], opnd[1], zero16());
+          else if ((j & 1) == 0) sacc = mfma32(kreg[ks], opnd[j % kPre], sacc);
+          else dpacc = mfma32(vreg[ks], opnd[j % kPre], dpacc);
+          if (j + kPre < 2 * KS) opnd[j % kPre] = load(j + kPre);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+#pragma unroll
+        for (int j = 0; j < 2 * KS - kPre; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
+        keep(sacc);
+        keep(dpacc);
+      }
+      fs = __builtin_amdgcn_readfirstlane(fs);
+      fp = __builtin_amdgcn_readfirstlane(fp);
+      ls = __builtin_amdgcn_readfirstlane(ls);
+      lp = __builtin_amdgcn_readfirstlane(lp);
+      const bool active = i < ntiles && wave_valid && !lex_less(ls, lp, kf_seq, kf_pos) &&
+                          !lex_less(kl_seq, INT_MAX, fs, fp);
+      const bool full = wave_complete && nrows == TR && fs == ls && fs == kf_seq && kf_seq == kl_seq &&
+                        fp >= kl_pos;
+      wg_barrier<kWaitLgkm>();
+      if (i == ntiles) break;
+      // half-step 2: softmax gradient of tile i -> exchange tiles of the group
+      int flag = 0;
+      if (active) {
+        const float lse2 = lse_n * kLog2e;
+        float p[16], ds[16];
+        if (full) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            p[r] = exp2_fast(fmaf(sacc[r], scale_log2, -lse2));
+            ds[r] = p[r] * (dpacc[r] - dl);
+          }
+        } else {
+          const bool row_ok = n < nrows && lse2 != kNegInf;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int kk = 32 * kg + 8 * r4 + 4 * hi;
+            const int4 ss = *reinterpret_cast<const int4*>(&kseq_s[kk]);
+            const int4 pp = *reinterpret_cast<const int4*>(&kpos_s[kk]);
+            const int sv[4] = {ss.x, ss.y, ss.z, ss.w};
+            const int pv[4] = {pp.x, pp.y, pp.z, pp.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * r4 + e;
+              const bool vis = row_ok & (sv[e] == rseq) & (pv[e] <= rpos);
+              const float pr = vis ? exp2_fast(fmaf(sacc[r], scale_log2, -lse2)) : 0.f;
+              p[r] = pr;
+              ds[r] = pr * (dpacc[r] - dl);
+            }
+          }
+        }
+        // P and dS enter the gradient MFMAs as bf16.  Where some P of the
+        // tile reaches kSplitP they enter as hi + lo bf16 pairs (lo = x - hi,
+        // a second MFMA on the same A operand): rows that give a key a large
+        // weight would otherwise carry bf16's 2^-9 relative rounding into the
+        // key's gradient with a large coefficient.  Below the threshold the
+        // dropped lo terms are at most kSplitP * 2^-9 each.
+        uint16_t* xrow = &X[kg][0][n * XS + 16 * hi];
+        bf16x8 ph[2], dh[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          ph[s2] = pack8(&p[8 * s2]);
+          dh[s2] = pack8(&ds[8 * s2]);
+          *reinterpret_cast<bf16x8*>(xrow + 8 * s2) = ph[s2];
+          *reinterpret_cast<bf16x8*>(xrow + XT + 8 * s2) = dh[s2];
+        }
+        f32x16 pv;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pv[r] = p[r];
+        const bool split = __any(max16_raw(0.f, pv) >= kSplitP);
+        flag = split ? 2 : 1;
+        if (split) {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            float pl[8], dl8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              pl[j] = p[8 * s2 + j] - static_cast<float>(ph[s2][j]);
+              dl8[j] = ds[8 * s2 + j] - static_cast<float>(dh[s2][j]);
+            }
+            *reinterpret_cast<bf16x8*>(xrow + 2 * XT + 8 * s2) = pack8(pl);
+            *reinterpret_cast<bf16x8*>(xrow + 3 * XT + 8 * s2) = pack8(dl8);
+          }
+        }
+      }
+      if (lane == 0) Xf[kg] = flag;
+    }
+    // every load of this workgroup has landed before its LDS is released
+    wg_barrier<kWaitAll>();
+  } else {
+    // ======================= consumer: dV, dK ===============================
+    f32x16 acc_v[MB], acc_k[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      acc_v[mb] = zero16();
+      acc_k[mb] = zero16();
+    }
+    // transposing reads of an exchange tile (one 32-column block)
+    const int xg = lane >> 4, xi = lane & 15;
+    const int xr0 = 4 * (xg >> 1) + (xi >> 2), xc0 = 16 * (xg & 1) + 4 * (xi & 3);
+    const int xo0 = xr0 * XS + xc0, xo1 = (xr0 + 8) * XS + xc0;
+    for (int i = 0; i <= ntiles; ++i) {
+      // tile i landed: only this wave's newest batch (tile i+1) may be in flight
+      if (i > 0) wg_barrier<wait_vm_lgkm<CROUNDS + 1>()>();
+      // half-step 1 (the producer's MFMAs): this iteration's loads, tile i+2
+      if (i < ntiles) issue((i + 2) % NST, min(i + 2, ntiles - 1));
+      // and the exchange tiles of tile i-1 into registers
+      int flag = 0;
+      bf16x8 pop[2] = {zero8(), zero8()}, dop[2] = {zero8(), zero8()};
+      bf16x8 plo[2] = {zero8(), zero8()}, dlo[2] = {zero8(), zero8()};
+      if (i > 0) {
+        flag = __builtin_amdgcn_readfirstlane(Xf[kg]);
+        if (flag > 0) {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            pop[s2] = tr_operand_at<XS>(&X[kg][0][0], 16 * s2, xo0, xo1);
+            dop[s2] = tr_operand_at<XS>(&X[kg][1][0], 16 * s2, xo0, xo1);
+          }
+          if (flag == 2) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+              plo[s2] = tr_operand_at<XS>(&X[kg][2][0], 16 * s2, xo0, xo1);
+              dlo[s2] = tr_operand_at<XS>(&X[kg][3][0], 16 * s2, xo0, xo1);
+            }
+          }
+        }
+      }
+      // the exchange tiles are in registers before the producer rewrites them
+      wg_barrier<kWaitLgkm>();
+      if (flag == 0) continue;
+      // half-step 2: dV^T += dO^T P, dK^T += Q^T dS over the 32 rows of tile
+      // i-1; A operands (transposed Q / dO tiles) loaded kPre MFMAs ahead
+      const uint16_t* prev = R[(i - 1) % NST];
+      constexpr int NSTEP = 4 * MB;   // (tensor, k-step, d-block)
       constexpr int kPre = 4;
-      constexpr int NSTEP = 4 * MB;
-      const uint16_t* Aown = At + 32 * rh * D;
-      const uint16_t* Apar = At + 32 * (1 - rh) * D;
-      const bf16x8 pb0 = Xh[(partner * 2 + 0) * 64 + lane];
-      const bf16x8 pb1 = Xh[(partner * 2 + 1) * 64 + lane];
       auto load = [&](int j) {
-        const int hh = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
-        return tr_operand<D>(hh == 0 ? Aown : Apar, lo_off, 16 * s2, mb);
+        const int tsr = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
+        return tr_operand<D>(prev + (tsr == 0 ? TS : 0), lo_off, 16 * s2, mb);
       };
       bf16x8 opnd[kPre];
 #pragma unroll
       for (int j = 0; j < kPre; ++j) opnd[j] = load(j);
 #pragma unroll
       for (int j = 0; j < NSTEP; ++j) {
-        const int hh = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
-        const bf16x8 b = hh == 0 ? own_h[s2] : (s2 == 0 ? pb0 : pb1);
-        acc[mb] = mfma32(opnd[j % kPre], b, acc[mb]);
+        const int tsr = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
+        if (tsr == 0) acc_v[mb] = mfma32(opnd[j % kPre], pop[s2], acc_v[mb]);
+        else acc_k[mb] = mfma32(opnd[j % kPre], dop[s2], acc_k[mb]);
         if (j + kPre < NSTEP) opnd[j % kPre] = load(j + kPre);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 + 2 * kPre, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre, 0);
 #pragma unroll
       for (int j = 0; j < NSTEP - kPre; ++j) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
-      return;
-    }
+      if (flag == 2) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const bool mine = h == rh;
-      const int f = mine ? own_f : par_f;
-      if (f == 0) continue;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int xi = (partner * 2 + s2) * 64 + lane;
-        const bf16x8 bh = mine ? own_h[s2] : Xh[xi];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const bf16x8 a = tr_operand<D>(At, lo_off, 32 * h + 16 * s2, mb);
-          acc[mb] = mfma32(a, bh, acc[mb]);
-        }
-        if (f == 2) {
-          const bf16x8 bl = mine ? own_l[s2] : Xl[xi];
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            const bf16x8 a = tr_operand<D>(At, lo_off, 32 * h + 16 * s2, mb);
-            acc[mb] = mfma32(a, bl, acc[mb]);
-          }
+        for (int j = 0; j < NSTEP; ++j) {
+          const int tsr = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
+          const bf16x8 a = tr_operand<D>(prev + (tsr == 0 ? TS : 0), lo_off, 16 * s2, mb);
+          if (tsr == 0) acc_v[mb] = mfma32(a, plo[s2], acc_v[mb]);
+          else acc_k[mb] = mfma32(a, dlo[s2], acc_k[mb]);
         }
       }
-    }
-  };
-
-  // ---- SDP: S = Q K^T, dP = dO V^T of tile i (ring stage st): lane (n = key,
-  // hi) register r holds row r0 + acc_row(r, hi).  The state below carries
-  // the tile to its SOFT step.
-  const int r0 = 32 * rh;
-  bool active = false, wave_full = false;
-  int nrows = 0, soft_st = 0;
-  f32x16 sacc = zero16(), dpacc = zero16();
-  // Visibility of tile i for this wave's key group and row half, from the
-  // sequence / position of the row half's first and last rows in the tile's
-  // meta: LDS reads issued right after the barrier that publishes the tile
-  // (vis_load) and evaluated after the dV / dK MFMAs (vis_eval), so that
-  // their latency stays hidden.
-  bool nx_active = false, nx_full = false;
-  int nx_nrows = 0;
-  int v_nr = 0, v_rl = 0, v_fs = 0, v_fp = 0, v_ls = 0, v_lp = 0;
-  bool v_some = false;
-  auto vis_load = [&](int i, int st) {
-    v_some = false;
-    v_nr = 0;
-    if (i >= ntiles) return;
-    const int t0 = tile_t0(i);
-    v_nr = (qhi - i * TPT - t0) * G;
-    if (r0 >= v_nr) return;
-    v_some = true;
-    v_rl = min(v_nr, r0 + 32) - 1;
-    const int* rseq_s = reinterpret_cast<const int*>(&Mr[st][2 * TR]);
-    const int* rpos_s = reinterpret_cast<const int*>(&Mr[st][3 * TR]);
-    v_fs = rseq_s[r0];
-    v_fp = rpos_s[r0];
-    v_ls = rseq_s[v_rl];
-    v_lp = rpos_s[v_rl];
-  };
-  auto vis_eval = [&]() {
-    nx_nrows = v_nr;
-    nx_active = __builtin_amdgcn_readfirstlane(
-        v_some && wave_valid && !lex_less(v_ls, v_lp, wf_seq, wf_pos) &&
-        !lex_less(wl_seq, INT_MAX, v_fs, v_fp));
-    nx_full = __builtin_amdgcn_readfirstlane(
-        v_some && wave_complete && v_rl == r0 + 31 && v_fs == v_ls && v_fs == wf_seq &&
-        wf_seq == wl_seq && v_fp >= wl_pos);
-  };
-
-  auto sdp = [&](int i, int st, auto dma_c, int dst, int di) {
-    constexpr bool kDMA = decltype(dma_c)::value;
-    static_assert(2 * LROUNDS + 1 < 2 * KS, "load rounds fit in the stream");
-    active = nx_active;
-    wave_full = nx_full;
-    nrows = nx_nrows;
-    soft_st = st;
-    if (i >= ntiles) {
-      sacc = zero16();
-      dpacc = zero16();
-      if (kDMA) {
+      // the MFMAs stay in this half-step
 #pragma unroll
-        for (int it = 0; it < LROUNDS; ++it) issue_round(dst, di, it);
-        issue_meta(dst, di);
+      for (int mb = 0; mb < MB; ++mb) {
+        keep(acc_v[mb]);
+        keep(acc_k[mb]);
       }
-      return;
     }
-    // 2*KS MFMAs (S then dP), operands loaded kPre steps ahead; computed for
-    // every wave so that the accumulators are redefined on every path (rows
-    // past the tile's end hold copies of its last row), used only if active
-    // S and dP MFMAs alternate (j even: S k-step j/2, j odd: dP), so that
-    // consecutive MFMAs are independent and the two accumulation chains
-    // cover each other's result latency.  Team 0 spreads the loads of the
-    // next tile over the stream (one round every other MFMA), so that no
-    // burst of them stalls the wave.
-    const uint16_t* cur = R[st];
-    constexpr int kPre = 8;
-    bf16x8 opnd[kPre];
-    auto load = [&](int j) {
-      return row_operand<D>(cur + (j & 1) * TS, lo_off, r0, j >> 1);
-    };
-#pragma unroll
-    for (int j = 0; j < kPre; ++j) opnd[j] = load(j);
-#pragma unroll
-    for (int j = 0; j < 2 * KS; ++j) {
-      const int ks = j >> 1;
-      if (j == 0) sacc = mfma32(opnd[0], kreg[0], zero16());
-      else if (j == 1) dpacc = mfma32(opnd[1], vreg[0], zero16());
-      else if ((j & 1) == 0) sacc = mfma32(opnd[j % kPre], kreg[ks], sacc);
-      else dpacc = mfma32(opnd[j % kPre], vreg[ks], dpacc);
-      if (j + kPre < 2 * KS) opnd[j % kPre] = load(j + kPre);
-      if (kDMA && (j & 1) && j / 2 < LROUNDS) issue_round(dst, di, j / 2);
-      if (kDMA && j == 2 * LROUNDS + 1) issue_meta(dst, di);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
-#pragma unroll
-    for (int j = 0; j < 2 * KS - kPre; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
-  };
-
-  // ---- SOFT: softmax gradient of the tile last passed to SDP: P, dS; own
-  // packs replace the previous tile's (already used by GRAD), partner-bound
-  // packs go to the exchange.
-  auto soft = [&]() {
-    own_f = 0;
-    if (active) {
-      const uint32_t* M = Mr[soft_st];
-      const float* lse_s = reinterpret_cast<const float*>(M);
-      const float* dl_s = reinterpret_cast<const float*>(M + TR);
-      const int* rseq_s = reinterpret_cast<const int*>(M + 2 * TR);
-      const int* rpos_s = reinterpret_cast<const int*>(M + 3 * TR);
-      float p[16], ds[16];
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int rb = r0 + 8 * r4 + 4 * hi;
-        const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[rb]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&dl_s[rb]);
-        const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-        if (wave_full) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * r4 + e;
-            p[r] = exp2_fast(fmaf(sacc[r], scale_log2, -lv[e]));
-            ds[r] = p[r] * (dpacc[r] - dv4[e]);
-          }
-        } else {
-          const int4 ss = *reinterpret_cast<const int4*>(&rseq_s[rb]);
-          const int4 pp = *reinterpret_cast<const int4*>(&rpos_s[rb]);
-          const int sv[4] = {ss.x, ss.y, ss.z, ss.w};
-          const int pv[4] = {pp.x, pp.y, pp.z, pp.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * r4 + e;
-            const bool vis = key_valid & (rb + e < nrows) & (lv[e] != kNegInf) &
-                             (sv[e] == kseq) & (pv[e] >= kpos);
-            const float pr = vis ? exp2_fast(fmaf(sacc[r], scale_log2, -lv[e])) : 0.f;
-            p[r] = pr;
-            ds[r] = pr * (dpacc[r] - dv4[e]);
-          }
-        }
-      }
-      // P and dS enter the gradient MFMAs as bf16.  Where some P of the
-      // block reaches kSplitP they enter as hi + lo bf16 pairs (lo = x - hi,
-      // a second MFMA on the same A operand): rows that give a key a large
-      // weight would otherwise carry bf16's 2^-9 relative rounding into the
-      // key's gradient with a large coefficient.  Below the threshold the
-      // dropped lo terms are at most kSplitP * 2^-9 each.
-      // own: P (rh = 0) or dS (rh = 1); partner-bound: the other one.  The
-      // partner-bound hi packs are written first, so that their LDS latency
-      // overlaps the rest of the step.
-      auto emit = [&](const float (&mine)[16], const float (&theirs)[16]) {
-        bf16x8 th[2];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          th[s2] = pack8(&theirs[8 * s2]);
-          Xh[(wave * 2 + s2) * 64 + lane] = th[s2];
-        }
-        f32x16 pv;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) pv[r] = p[r];
-        const bool split = __any(max16_raw(0.f, pv) >= kSplitP);
-        own_f = split ? 2 : 1;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) own_h[s2] = pack8(&mine[8 * s2]);
-        if (split) {
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            float ol[8], tl[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              ol[j] = mine[8 * s2 + j] - static_cast<float>(own_h[s2][j]);
-              tl[j] = theirs[8 * s2 + j] - static_cast<float>(th[s2][j]);
-            }
-            own_l[s2] = pack8(ol);
-            Xl[(wave * 2 + s2) * 64 + lane] = pack8(tl);
-          }
-        }
-      };
-      if (rh) emit(ds, p);
-      else emit(p, ds);
-    }
-    if (lane == 0) Xf[wave] = own_f;
-  };
-
-  // Iterations run 0 .. ntiles; tile i sits in stage i % 3.  The last
-  // iteration only finishes tile ntiles-1.
-  if (team == 0 && ntiles > 0) {
-#pragma unroll
-    for (int it = 0; it < LROUNDS; ++it) issue_round(0, 0, it);
-    issue_meta(0, 0);
-  }
-  if (team == 1) wg_barrier<kWaitLgkm>();
-  int sc = 0;
-  for (int i = 0; i <= ntiles; ++i) {
-    const int sn = sc == 2 ? 0 : sc + 1;
-    const int sp = sc == 0 ? 2 : sc - 1;
-    // MFMA window: tile i landed (team 0 waited for its loads); stage sn
-    // (tile i-2) is free
     wg_barrier<kWaitAll>();
-    vis_load(i, sc);
-    if (i >= 1) grad(R[sp]);
-    vis_eval();
-    if (team == 0 && i + 1 < ntiles)
-      sdp(i, sc, BoolC<true>(), sn, i + 1);
-    else
-      sdp(i, sc, BoolC<false>(), 0, 0);
-    // VALU window
-    wg_barrier<kWaitLgkm>();
-    soft();
-    sc = sn;
-  }
-  if (team == 0) wg_barrier<kWaitLgkm>();
-
-  if (!key_valid) return;
-  const size_t obase = (static_cast<size_t>(my_key) * hkv + g) * D;
-  float* const out = rh ? dk : dv;
-  const float sc_out = rh ? scale : 1.f;
+    // ---- store: output column n holds key kmap(n) ----------------------
+    const int my_key = wk0 + kmap(n);
+    if (my_key < nk) {
+      const size_t obase = (static_cast<size_t>(my_key) * hkv + g) * D;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      float4* po = reinterpret_cast<float4*>(out + obase + mb * 32 + 8 * gq + 4 * hi);
-      float4 a = *po;
-      a.x += sc_out * acc[mb][4 * gq + 0];
-      a.y += sc_out * acc[mb][4 * gq + 1];
-      a.z += sc_out * acc[mb][4 * gq + 2];
-      a.w += sc_out * acc[mb][4 * gq + 3];
-      *po = a;
+        for (int gq = 0; gq < 4; ++gq) {
+          float4* pv = reinterpret_cast<float4*>(dv + obase + mb * 32 + 8 * gq + 4 * hi);
+          float4* pk = reinterpret_cast<float4*>(dk + obase + mb * 32 + 8 * gq + 4 * hi);
+          float4 a = *pv, b = *pk;
+          a.x += acc_v[mb][4 * gq + 0];
+          a.y += acc_v[mb][4 * gq + 1];
+          a.z += acc_v[mb][4 * gq + 2];
+          a.w += acc_v[mb][4 * gq + 3];
+          b.x += scale * acc_k[mb][4 * gq + 0];
+          b.y += scale * acc_k[mb][4 * gq + 1];
+          b.z += scale * acc_k[mb][4 * gq + 2];
+          b.w += scale * acc_k[mb][4 * gq + 3];
+          *pv = a;
+          *pk = b;
+        }
     }
+  }
 }
 
 template <int D, int G>
