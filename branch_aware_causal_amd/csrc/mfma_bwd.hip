@@ -563,7 +563,9 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
           else dpacc = mfma32(vreg[ks], opnd[j % kPre], dpacc);
           if (j + kPre < 2 * KS) opnd[j % kPre] = load(j + kPre);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+        // pin the order: the 8 meta reads and the first kPre operands, then
+        // one MFMA and the next operand
+        __builtin_amdgcn_sched_group_barrier(0x100, 8 + kPre, 0);
 #pragma unroll
         for (int j = 0; j < 2 * KS - kPre; ++j) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
