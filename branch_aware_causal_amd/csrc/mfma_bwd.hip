@@ -536,10 +536,6 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
         nrows = (qhi - i * TPT - t0) * G;
         const int* rseq_s = reinterpret_cast<const int*>(&Mr[st][2 * MS]);
         const int* rpos_s = reinterpret_cast<const int*>(&Mr[st][3 * MS]);
-        fs = rseq_s[0];
-        fp = rpos_s[0];
-        ls = rseq_s[nrows - 1];
-        lp = rpos_s[nrows - 1];
         lse_n = reinterpret_cast<const float*>(&Mr[st][0])[n];
         dl = reinterpret_cast<const float*>(&Mr[st][MS])[n];
         rseq = rseq_s[n];
@@ -563,9 +559,9 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
           else dpacc = mfma32(vreg[ks], opnd[j % kPre], dpacc);
           if (j + kPre < 2 * KS) opnd[j % kPre] = load(j + kPre);
         }
-        // pin the order: the 8 meta reads and the first kPre operands, then
+        // pin the order: the 4 meta reads and the first kPre operands, then
         // one MFMA and the next operand
-        __builtin_amdgcn_sched_group_barrier(0x100, 8 + kPre, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 + kPre, 0);
 #pragma unroll
         for (int j = 0; j < 2 * KS - kPre; ++j) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -575,10 +571,13 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
         keep(sacc);
         keep(dpacc);
       }
-      fs = __builtin_amdgcn_readfirstlane(fs);
-      fp = __builtin_amdgcn_readfirstlane(fp);
-      ls = __builtin_amdgcn_readfirstlane(ls);
-      lp = __builtin_amdgcn_readfirstlane(lp);
+      // the tile's first and last rows, from the lanes that hold them
+      if (i < ntiles) {
+        fs = __builtin_amdgcn_readlane(rseq, 0);
+        fp = __builtin_amdgcn_readlane(rpos, 0);
+        ls = __builtin_amdgcn_readlane(rseq, nrows - 1);
+        lp = __builtin_amdgcn_readlane(rpos, nrows - 1);
+      }
       const bool active = i < ntiles && wave_valid && !lex_less(ls, lp, kf_seq, kf_pos) &&
                           !lex_less(kl_seq, INT_MAX, fs, fp);
       const bool full = wave_complete && nrows == TR && fs == ls && fs == kf_seq && kf_seq == kl_seq &&
