@@ -33,7 +33,8 @@ constexpr int NW = 8;
 // dq kernel layout:
 //   * A workgroup has 8 waves and owns TPB = 8 * 32/G consecutive query
 //     tokens of one kv-head group; wave w owns 32 (token, head) rows, one per
-//     lane pair (n, n+32).  Q stays in registers, the wave's dO rows in LDS.
+//     lane pair (n, n+32).  Q and dO stay in registers (B operands of S^T
+//     and dP^T), so every MFMA of the stream reads one operand from LDS.
 //   * Keys stream through LDS in tiles of 64, copied straight from global
 //     memory (K in a ring of three, V in a ring of two).  The keys a row sees
 //     are one index interval of the (seq, pos)-sorted shard, found by binary
@@ -66,7 +67,6 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[3][BN * D];   // keys x d, swizzled
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[NW][32 * D];  // each wave's dO rows
 
   const float scale_log2 = scale * kLog2e;
   const int nblk_tok = (nq + TPB - 1) / TPB;
@@ -97,17 +97,14 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
   const int hi_k = upper_bound_sp(k_seq, k_pos, nk, q_seq[blast], q_pos[blast]);
   const int ntiles = hi_k > lo ? (hi_k - lo + BN - 1) / BN : 0;
 
-  // Q operands stay in registers; the wave's dO rows go to LDS (read back as
-  // the B operand of dP^T = V dO^T) to keep the wave within 256 registers.
-  bf16x8 qreg[KS];
-  uint16_t* my_do = dOs[wave];
+  // Q and dO rows in registers: the B operands of S^T = K Q^T and dP^T = V dO^T.
+  bf16x8 qreg[KS], doreg[KS];
   {
     const size_t off = (static_cast<size_t>(my_tok) * hq + my_head) * D + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qreg[ks] = row_valid ? *reinterpret_cast<const bf16x8*>(q + off + 16 * ks) : zero8();
-      const bf16x8 dv = row_valid ? *reinterpret_cast<const bf16x8*>(dout + off + 16 * ks) : zero8();
-      *reinterpret_cast<bf16x8*>(my_do + lo_off.row[ks]) = dv;
+      doreg[ks] = row_valid ? *reinterpret_cast<const bf16x8*>(dout + off + 16 * ks) : zero8();
     }
   }
   f32x16 dqacc[MB];
@@ -119,15 +116,14 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
   // of a tile, i.e. physical chunk p of key row r; it fetches logical chunk
   // swz(r, p) (the swizzle is an involution).  Keys past the end re-read the
   // last key; they and keys past hi_k are masked by index.
+  // Round `it` covers key rows RPR*it + r0 (r0 = slot's row in round 0);
+  // the swizzle depends on the row modulo 16 only, so one column offset
+  // serves every round.
   constexpr int ROUNDS = BN * CPR / 256;
-  uint32_t lane_row[ROUNDS], lane_col[ROUNDS];
-#pragma unroll
-  for (int it = 0; it < ROUNDS; ++it) {
-    const int slot = (it * 4 + (wave & 3)) * 64 + lane;
-    const int r = slot / CPR, pc = slot % CPR;
-    lane_row[it] = r;
-    lane_col[it] = 2u * (g * D + 8 * swz<D>(r, pc));
-  }
+  constexpr int RPR = 256 / CPR;     // key rows per round
+  static_assert(RPR % 16 == 0, "rounds keep the row's swizzle");
+  const int lane_r0 = ((wave & 3) * 64 + lane) / CPR;
+  const uint32_t lane_col = 2u * (g * D + 8 * swz<D>(lane_r0, ((wave & 3) * 64 + lane) % CPR));
   const uint32_t krow_bytes = static_cast<uint32_t>(hkv * D * 2);
   auto issue_rows = [&](const uint16_t* src, const uint16_t* dst_tile, int j0) {
     const char* base = reinterpret_cast<const char*>(src) + static_cast<size_t>(j0) * krow_bytes;
@@ -135,7 +131,7 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
 #pragma unroll
     for (int it = 0; it < ROUNDS; ++it) {
       const uint32_t off =
-          static_cast<uint32_t>(min(static_cast<int>(lane_row[it]), rmax)) * krow_bytes + lane_col[it];
+          static_cast<uint32_t>(min(lane_r0 + RPR * it, rmax)) * krow_bytes + lane_col;
       dma_b128(base, off, lds_addr(dst_tile) + (it * 4 + (wave & 3)) * 64 * 16);
     }
   };
@@ -177,7 +173,7 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
   // tile (4*MB MFMAs, transposed K operands), then S^T = K Q^T and
   // dP^T = V dO^T for this tile (4*KS MFMAs, alternating).  LDS operands are
   // read kPre MFMAs ahead.
-  constexpr int kPre = 4;
+  constexpr int kPre = 2;
   auto mfma_stream = [&](auto dq_c, auto s_c, const uint16_t* kprev, const uint16_t* kt,
                          const uint16_t* vt) {
     constexpr bool kDQ = decltype(dq_c)::value, kS = decltype(s_c)::value;
@@ -191,16 +187,10 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
       const int i = j - NP, kb = (i / 2) % 2, ks = i / 4;
       return row_operand<D>((i & 1) ? vt : kt, lo_off, kb * 32, ks);
     };
-    auto load_b = [&](int j) {   // dO operand of a dP step
-      const int ks = (j - NP) / 4;
-      return row_operand<D>(my_do, lo_off, 0, ks);
-    };
-    auto is_dp = [&](int j) { return j >= NP && ((j - NP) & 1); };
-    bf16x8 opa[kPre], opb[kPre];
+    bf16x8 opa[kPre];
 #pragma unroll
     for (int j = 0; j < kPre; ++j) {
       opa[j] = load_a(j);
-      if (is_dp(j)) opb[j] = load_b(j);
     }
     if (kS) {
 #pragma unroll
@@ -217,27 +207,26 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
       } else {
         const int i = j - NP, kb = (i / 2) % 2, ks = i / 4;
         if (i & 1)
-          dpacc[kb] = mfma32(opa[j % kPre], opb[j % kPre], dpacc[kb]);
+          dpacc[kb] = mfma32(opa[j % kPre], doreg[ks], dpacc[kb]);
         else
           sacc[kb] = mfma32(opa[j % kPre], qreg[ks], sacc[kb]);
       }
       if (j + kPre < N) {
         opa[j % kPre] = load_a(j + kPre);
-        if (is_dp(j + kPre)) opb[j % kPre] = load_b(j + kPre);
       }
     }
     // pin the order: the first kPre steps' operands, then one MFMA and the
-    // operands of the step kPre ahead (2 LDS reads for dQ and dP steps, 1 for S)
+    // operand of the step kPre ahead (2 LDS reads for a dQ step, 1 for S / dP)
     static_assert(NP == 0 || NP >= kPre, "prefetch covers one operand kind");
     static_assert(kPre % 2 == 0, "S / dP alternate");
     if constexpr (NP > 0)
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre, 0);
     else
-      __builtin_amdgcn_sched_group_barrier(0x100, 3 * kPre / 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
 #pragma unroll
     for (int j = 0; j < N; ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (j + kPre < NP || (j + kPre < N && is_dp(j + kPre)))
+      if (j + kPre < NP)
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       else if (j + kPre < N)
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
