@@ -72,8 +72,9 @@ class Timer:
         self.total = {}
         self.count = {}
         self.work = {}
+        self.bytes = {}
 
-    def __call__(self, name, work, fn, *args, **kw):
+    def __call__(self, name, work, fn, *args, nbytes=0, **kw):
         if not self.enabled:
             return fn(*args, **kw)
         a = self.torch.cuda.Event(enable_timing=True)
@@ -81,13 +82,14 @@ class Timer:
         a.record(self.stream)
         fn(*args, **kw)
         b.record(self.stream)
-        self.pending.append((name, work, a, b))
+        self.pending.append((name, work, nbytes, a, b))
 
     def collect(self):
-        for name, work, a, b in self.pending:
+        for name, work, nbytes, a, b in self.pending:
             self.total[name] = self.total.get(name, 0.0) + a.elapsed_time(b) / 1e3
             self.count[name] = self.count.get(name, 0) + 1
             self.work[name] = self.work.get(name, 0.0) + work
+            self.bytes[name] = self.bytes.get(name, 0.0) + nbytes
         self.pending = []
 
 
@@ -134,6 +136,15 @@ def build_step(torch, api, ring, w, st, t, dev, timer):
     kb_branch = 2 * 2 * nb * hkv * d * 2   # branch fwd bytes are reported, not priced
     work = dict(pairs=total_pairs, local_pairs=local, flops=total_pairs * hq * 14 * d,
                 fwd_flops=total_pairs * hq * 4 * d, bwd_flops=total_pairs * hq * 10 * d)
+    # algorithmic HBM bytes of the bandwidth-bound launches (each tensor element
+    # read or written once; the merge into the accumulators and the bf16 output
+    # are fused into the branch forward)
+    qrow, krow = hq * d, hkv * d
+    bytes_branch_fwd = nb * (2 * qrow + 2 * 2 * krow + 2 * 4 * qrow + 2 * 4 * hq + 2 * qrow)
+    bytes_branch_bwd = nb * (2 * 2 * qrow + 2 * 2 * krow + 2 * 4 * hq + 2 * 4 * qrow + 2 * 2 * 4 * krow)
+    bytes_delta = lambda n: n * (4 * qrow + 2 * qrow + 4 * hq)
+    work["bytes"] = dict(branch_fwd=bytes_branch_fwd, branch_bwd=bytes_branch_bwd,
+                         delta=bytes_delta(nm) + bytes_delta(nb))
     i32 = lambda a: torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32))
     cu, bcu, anc = st.cu_seqlens, st.branch_cu, st.branch_anchor
 
@@ -166,10 +177,12 @@ def build_step(torch, api, ring, w, st, t, dev, timer):
         # (a5, a6) rank-local branch part, final merge and bf16 rounding
         timer("branch_fwd", local * hq * 4 * d, api.attn_branch_fwd, ri.q_br, ri.kb, ri.vb, lbcu,
               ri.max_branch_len, ri.kind, bufs["o_br_acc"], bufs["lse_br"], api.MERGE,
-              o_out=bufs["o_br"])
+              o_out=bufs["o_br"], nbytes=bytes_branch_fwd)
         # (a7) Delta
-        timer("delta", 0, api.attn_bwd_delta, bufs["o_main_acc"], ri.do_main, bufs["delta_main"])
-        timer("delta", 0, api.attn_bwd_delta, bufs["o_br_acc"], ri.do_br, bufs["delta_br"])
+        timer("delta", 0, api.attn_bwd_delta, bufs["o_main_acc"], ri.do_main, bufs["delta_main"],
+              nbytes=bytes_delta(nm))
+        timer("delta", 0, api.attn_bwd_delta, bufs["o_br_acc"], ri.do_br, bufs["delta_br"],
+              nbytes=bytes_delta(nb))
         for key in ("dq_main", "dq_br", "dkb", "dvb"):
             bufs[key].zero_()
         for s in range(C):
@@ -191,7 +204,7 @@ def build_step(torch, api, ring, w, st, t, dev, timer):
         # (a9) branch backward
         timer("branch_bwd", local * hq * 10 * d, api.attn_branch_bwd, ri.q_br, ri.kb, ri.vb, lbcu,
               ri.max_branch_len, ri.kind, ri.do_br, bufs["lse_br"], bufs["delta_br"],
-              bufs["dq_br"], bufs["dkb"], bufs["dvb"])
+              bufs["dq_br"], bufs["dkb"], bufs["dvb"], nbytes=bytes_branch_bwd)
 
     return step, work, ri, pl, bufs
 
@@ -278,7 +291,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="eagle3_256k")
-    ap.add_argument("--cpu-anchors", type=int, default=6,
+    ap.add_argument("--cpu-anchors", type=int, default=12,
                     help="anchors whose rows the CPU oracle processes for cpu_baseline (0: skip)")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
@@ -328,6 +341,10 @@ def main():
                      avg_ms=round(tot / n * 1e3, 4))
         if timer.work[name] > 0:
             entry["tflops"] = round(timer.work[name] / tot / 1e12, 1)
+        if timer.bytes.get(name, 0) > 0:
+            gbs = timer.bytes[name] / tot / 1e9
+            entry.update(hbm_gbs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4),
+                         bytes_per_launch=int(timer.bytes[name] / n))
         kernels[name] = entry
         log(f"  {name:14s} {entry}")
     mfma = {k: v for k, v in timer.total.items() if k in KERNEL_SOURCES}
@@ -350,6 +367,30 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy of {nbytes} bytes done")
         del a, b
+
+    # the standalone online-softmax merge (fused into every forward epilogue of
+    # the step above), timed on the branch rows' fp32 accumulators: two fp32
+    # O and two lse read, one O and one lse written per (row, head)
+    nb = bufs["o_br_acc"].shape[0]
+    o_part = torch.zeros_like(bufs["o_br_acc"])
+    lse_part = torch.zeros_like(bufs["lse_br"])
+    merge_ms = []
+    for rep in range(4):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        api.lse_merge(bufs["o_br_acc"], bufs["lse_br"], o_part, lse_part)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        if rep > 0:
+            merge_ms.append(ev0.elapsed_time(ev1))
+    del o_part, lse_part
+    merge_bytes = nb * w.hq * (3 * 4 * w.d + 3 * 4)
+    merge_s = float(np.median(merge_ms)) / 1e3
+    kernels["lse_merge_standalone"] = dict(
+        avg_ms=round(merge_s * 1e3, 4), rows=nb, heads=w.hq, bytes_per_launch=merge_bytes,
+        hbm_gbs=round(merge_bytes / merge_s / 1e9, 1),
+        hbm_frac=round(merge_bytes / merge_s / 1e9 / PEAK_HBM_GBS, 4))
+    log(f"  lse_merge (standalone, {nb} rows x {w.hq} heads) {kernels['lse_merge_standalone']}")
 
     cpu = None
     if args.cpu_anchors > 0:
