@@ -3,6 +3,7 @@
 // device work and reports problems through a status code plus a thread-local
 // message; nothing here throws or aborts.
 
+#include <initializer_list>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -63,6 +64,14 @@ static bac_status check_count(const char* fn, const char* what, int32_t n, int32
   return BAC_OK;
 }
 
+// Tensors are read and written with 16-byte vector accesses.
+static bac_status check_aligned(const char* fn, std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && (reinterpret_cast<uintptr_t>(p) & 15u))
+      return fail(BAC_EINVAL, "%s: tensor pointer %p is not 16-byte aligned", fn, p);
+  return BAC_OK;
+}
+
 #define BAC_TRY(expr)              \
   do {                             \
     bac_status _st = (expr);       \
@@ -119,6 +128,7 @@ bac_status attn_main_fwd(const void* q, const int32_t* q_seq, const int32_t* q_p
   if (mode != BAC_WRITE && mode != BAC_MERGE) return fail(BAC_EINVAL, "%s: unknown mode %d", fn, mode);
   if (nq > 0 && (!o_acc || !lse)) return fail(BAC_EINVAL, "%s: null o_acc or lse", fn);
   if (nq == 0) return BAC_OK;
+  BAC_TRY(check_aligned(fn, {q, k, v, o_acc, o_out}));
   MainArgs a{};
   a.q = q; a.q_seq = q_seq; a.q_pos = q_pos; a.nq = nq;
   a.k = k; a.v = v; a.k_seq = k_seq; a.k_pos = k_pos; a.nk = nk;
@@ -141,6 +151,7 @@ bac_status attn_branch_fwd(const void* qb, const void* kb, const void* vb, int32
   if (mode != BAC_WRITE && mode != BAC_MERGE) return fail(BAC_EINVAL, "%s: unknown mode %d", fn, mode);
   if (nb > 0 && (!o_acc || !lse)) return fail(BAC_EINVAL, "%s: null o_acc or lse", fn);
   if (nb == 0 || num_branches == 0) return BAC_OK;
+  BAC_TRY(check_aligned(fn, {qb, kb, vb, o_acc, o_out}));
   BranchArgs a{};
   a.qb = qb; a.kb = kb; a.vb = vb; a.nb = nb;
   a.branch_cu = branch_cu; a.num_branches = num_branches; a.max_len = max_branch_len;
@@ -164,6 +175,7 @@ bac_status lse_merge(float* o_acc, float* lse_acc, const float* o_part, const fl
     return fail(BAC_EINVAL, "%s: null accumulator or part", fn);
   if (n > 0 && o_acc == o_part) return fail(BAC_EINVAL, "%s: o_part aliases o_acc", fn);
   if (n == 0) return BAC_OK;
+  BAC_TRY(check_aligned(fn, {o_acc, o_part, o_out}));
   return hip_status(launch_lse_merge(o_acc, lse_acc, o_part, lse_part, n, hq, d, out_dt, o_out,
                                      static_cast<hipStream_t>(stream)),
                     fn);
@@ -180,6 +192,7 @@ bac_status attn_bwd_delta(const void* o, bac_dtype o_dt, const void* dout, bac_d
     return fail(BAC_EINVAL, "%s: unknown dtype", fn);
   if (n > 0 && (!o || !dout || !delta)) return fail(BAC_EINVAL, "%s: null pointer", fn);
   if (n == 0) return BAC_OK;
+  BAC_TRY(check_aligned(fn, {o, dout}));
   return hip_status(launch_delta(o, o_dt, dout, dt, n, hq, d, delta, static_cast<hipStream_t>(stream)),
                     fn);
 }
@@ -198,6 +211,7 @@ static bac_status main_bwd_impl(const char* fn, int part, const void* q, const i
   if (nk > 0 && part != 1 && (!dk_acc || !dv_acc))
     return fail(BAC_EINVAL, "%s: null dk_acc or dv_acc", fn);
   if (nq == 0 || nk == 0) return BAC_OK;
+  BAC_TRY(check_aligned(fn, {q, k, v, dout, dq_acc, dk_acc, dv_acc}));
   MainArgs a{};
   a.q = q; a.q_seq = q_seq; a.q_pos = q_pos; a.nq = nq;
   a.k = k; a.v = v; a.k_seq = k_seq; a.k_pos = k_pos; a.nk = nk;
@@ -250,6 +264,7 @@ bac_status attn_branch_bwd(const void* qb, const void* kb, const void* vb, int32
   if (nb > 0 && (!doutb || !lseb || !deltab || !dqb_acc || !dkb_acc || !dvb_acc))
     return fail(BAC_EINVAL, "%s: null gradient argument", fn);
   if (nb == 0 || num_branches == 0) return BAC_OK;
+  BAC_TRY(check_aligned(fn, {qb, kb, vb, doutb, dqb_acc, dkb_acc, dvb_acc}));
   BranchArgs a{};
   a.qb = qb; a.kb = kb; a.vb = vb; a.nb = nb;
   a.branch_cu = branch_cu; a.num_branches = num_branches; a.max_len = max_branch_len;

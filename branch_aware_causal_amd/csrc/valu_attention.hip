@@ -76,10 +76,69 @@ __device__ __forceinline__ void online_update(float x, const float (&v)[EPL], fl
   m2 = mn;
 }
 
+// Eight consecutive elements of a row as fp32 (16-byte loads for bf16, two
+// for fp32); the offset is a multiple of 8 elements.
+template <typename T>
+__device__ __forceinline__ void load8(const T* base, size_t off, float (&x)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint4 w = *reinterpret_cast<const uint4*>(base + off);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(u[i] << 16);
+      x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(base + off);
+    const float4 b = *reinterpret_cast<const float4*>(base + off + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T* base, size_t off, const float (&x)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    uint4 w;
+    w.x = pack_bf16x2(x[0], x[1]);
+    w.y = pack_bf16x2(x[2], x[3]);
+    w.z = pack_bf16x2(x[4], x[5]);
+    w.w = pack_bf16x2(x[6], x[7]);
+    *reinterpret_cast<uint4*>(base + off) = w;
+  } else {
+    *reinterpret_cast<float4*>(base + off) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(base + off + 4) = make_float4(x[4], x[5], x[6], x[7]);
+  }
+}
+
+// Sum over each aligned group of N lanes (N = 8 or 16), every lane of the
+// group receiving it, with DPP moves inside the 16-lane rows: swap within
+// pairs, then within quads, then mirror the half-rows, then the rows.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16, "DPP row moves stay inside 16-lane rows");
+  auto mov = [](float v, int ctrl) -> float {
+    switch (ctrl) {
+      case 0: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+      case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+      case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
+      default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true));
+    }
+  };
+  x += mov(x, 0);   // quad_perm [1,0,3,2]: lane ^ 1
+  x += mov(x, 1);   // quad_perm [2,3,0,1]: lane ^ 2
+  x += mov(x, 2);   // row_half_mirror: lane i <-> 7 - i within each 8
+  if constexpr (N == 16) x += mov(x, 3);   // row_mirror: lane i <-> 15 - i
+  return x;
+}
+
 // ---------------------------------------------------------------------------
 // Branch forward: wave w of block b handles branch a = 4b + w, kv-head
 // blockIdx.y, i.e. rows (t, h) for every token t of the branch and every
-// q-head h of the group.  Any branch length is handled (no LDS).
+// q-head h of the group.  A row occupies D/8 lanes (eight elements each, so
+// every access is 16 or 32 contiguous bytes per lane) and a pass covers
+// 64/(D/8) q-heads of the group at once; dot products are DPP sums inside
+// each row's lanes.  Any branch length is handled (no LDS).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void branch_fwd_kernel(const T* __restrict__ qb,
@@ -89,38 +148,66 @@ __global__ __launch_bounds__(256) void branch_fwd_kernel(const T* __restrict__ q
                                                          int bidir, int hq, int hkv,
                                                          float scale_log2, float* o_acc,
                                                          float* lse_acc, int mode, T* o_out) {
-  constexpr int EPL = D / 64;
+  constexpr int LPR = D / 8;       // lanes per row
+  constexpr int RPW = 64 / LPR;    // q-heads per pass
   const int lane = threadIdx.x & 63;
   const int a = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (a >= A) return;
   const int g = blockIdx.y;
   const int G = hq / hkv;
+  const int r = lane / LPR, col = 8 * (lane % LPR);
   const int t0 = max(0, min(bcu[a], nb));
   const int t1 = max(t0, min(bcu[a + 1], nb));
   const int len = t1 - t0;
-  for (int t = 0; t < len; ++t) {
-    const int kend = bidir ? len : t + 1;
-    for (int hl = 0; hl < G; ++hl) {
-      const int h = g * G + hl;
-      const size_t qoff = (static_cast<size_t>(t0 + t) * hq + h) * D;
-      float q[EPL], o[EPL];
-      load_lane<T, EPL>(qb, qoff, lane, q);
+  for (int c0 = 0; c0 < G; c0 += RPW) {
+    // lanes past the group's last q-head repeat its first and store nothing
+    const bool row_ok = c0 + r < G;
+    const int h = g * G + (row_ok ? c0 + r : 0);
+    for (int t = 0; t < len; ++t) {
+      const int kend = bidir ? len : t + 1;
+      const size_t qoff = (static_cast<size_t>(t0 + t) * hq + h) * D + col;
+      float q[8], o[8];
+      load8<T>(qb, qoff, q);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+      for (int e = 0; e < 8; ++e) o[e] = 0.f;
       float m2 = kNegInf, l = 0.f;
       for (int u = 0; u < kend; ++u) {
-        const size_t koff = (static_cast<size_t>(t0 + u) * hkv + g) * D;
-        float kk[EPL], vv[EPL];
-        load_lane<T, EPL>(kb, koff, lane, kk);
-        load_lane<T, EPL>(vb, koff, lane, vv);
+        const size_t koff = (static_cast<size_t>(t0 + u) * hkv + g) * D + col;
+        float kk[8], vv[8];
+        load8<T>(kb, koff, kk);
+        load8<T>(vb, koff, vv);
         float dot = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) dot += q[e] * kk[e];
-        dot = wave_sum(dot);
-        online_update<EPL>(dot * scale_log2, vv, m2, l, o);
+        for (int e = 0; e < 8; ++e) dot = fmaf(q[e], kk[e], dot);
+        dot = group_sum<LPR>(dot);
+        online_update<8>(dot * scale_log2, vv, m2, l, o);
       }
-      finish_row<T, EPL>(o, m2, l, qoff, static_cast<size_t>(h) * nb + t0 + t, mode, o_acc,
-                         lse_acc, o_out, lane);
+      if (!row_ok) continue;
+      // normalise, merge into the accumulators if asked, store
+      float lse2, inv;
+      if (l > 0.f) {
+        lse2 = m2 + log2_fast(l);
+        inv = 1.f / l;
+      } else {
+        lse2 = kNegInf;
+        inv = 0.f;
+      }
+      const size_t lidx = static_cast<size_t>(h) * nb + t0 + t;
+      float res[8];
+      float lnew = lse2;
+      if (mode == 1) {
+        float wa, wb, prev[8];
+        merge_weights_log2(lse_acc[lidx] * kLog2e, lse2, wa, wb, lnew);
+        load8<float>(o_acc, qoff, prev);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) res[e] = wa * prev[e] + wb * (o[e] * inv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) res[e] = o[e] * inv;
+      }
+      store8<float>(o_acc, qoff, res);
+      if (o_out) store8<T>(o_out, qoff, res);
+      if (col == 0) lse_acc[lidx] = (lnew == kNegInf) ? kNegInf : lnew * kLn2;
     }
   }
 }

@@ -20,7 +20,10 @@
  * Ownership: every buffer belongs to the caller; the library allocates
  *            nothing and keeps no pointer after returning.
  * Memory:    "device" pointers are HIP device memory; "host" pointers are
- *            ordinary host memory.  Index arrays are int32.
+ *            ordinary host memory.  Index arrays are int32.  Tensor pointers
+ *            (q, k, v, dout, o_out and the fp32 o / dq / dk / dv buffers)
+ *            must be 16-byte aligned (BAC_EINVAL otherwise); index and lse
+ *            arrays need only their element alignment.
  * Streams:   `stream` is a hipStream_t (NULL = the null stream).  Device work
  *            is enqueued on it and the call returns without synchronising.
  * Layouts:   packed token-major ("THD"): queries [n, hq, d], keys/values

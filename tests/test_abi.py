@@ -76,6 +76,19 @@ def test_main_fwd_rejects_bad_arguments(lib, over, code, needle):
     assert needle in _lib.last_error()
 
 
+def test_misaligned_tensors_are_rejected_before_launch(lib):
+    # every other argument valid; tensor pointers off a 16-byte boundary
+    from branch_aware_causal_amd import _lib
+    assert _call_main_fwd(lib, q=24, k=32, v=48, o_acc=64) == -1
+    assert "16-byte aligned" in _lib.last_error()
+    vp = C.c_void_p
+    st = lib.attn_branch_fwd(vp(16), vp(40), vp(48), 8, vp(4), 2, 3, 0, 8, 2, 128, 1, 0.1, vp(64),
+                             vp(4), 0, vp(None), vp(None))
+    assert st == -1 and "16-byte aligned" in _lib.last_error()
+    st = lib.lse_merge(vp(16), vp(4), vp(36), vp(4), 4, 8, 128, 1, vp(None), vp(None))
+    assert st == -1 and "16-byte aligned" in _lib.last_error()
+
+
 def test_empty_calls_are_noops(lib):
     # nothing to do -> success without touching any pointer or device
     assert _call_main_fwd(lib, nq=0, q=None, q_seq=None, q_pos=None, o_acc=None, lse=None) == 0
