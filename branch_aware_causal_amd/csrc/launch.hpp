@@ -77,9 +77,4 @@ hipError_t launch_delta(const void* o, int o_dt, const void* dout, int dt, int n
 hipError_t launch_check_index(const int32_t* seq, const int32_t* pos, int n, int strict,
                               int32_t* bad, hipStream_t s);
 
-// Bytes of dynamic LDS the branch backward needs per workgroup.
-inline size_t branch_bwd_lds_bytes(int max_len, int d) {
-  return static_cast<size_t>(max_len) * d * 2 * sizeof(float);
-}
-
 }  // namespace bac

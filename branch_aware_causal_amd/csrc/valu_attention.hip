@@ -4,8 +4,9 @@
 //   * the fp32 main-attention path (one wave per (row, head); fp32 has no
 //     MFMA product worth the packing at the sizes it serves).
 // Branch work is a few keys per row and HBM-bound, so one wave handles one
-// (branch, kv-head) with lanes spread over the head dimension; dot products
-// are wave reductions.  All index reads are range-clamped.
+// (branch, kv-head), each row spread over D/8 lanes with several q-heads of
+// the group side by side; dot products are DPP sums inside a row's lanes.
+// All index reads are range-clamped.
 
 #include <climits>
 
@@ -138,14 +139,14 @@ __device__ __forceinline__ float group_sum(float x) {
 // q-head h of the group.  A row occupies D/8 lanes (eight elements each, so
 // every access is 16 or 32 contiguous bytes per lane) and a pass covers
 // 64/(D/8) q-heads of the group at once; dot products are DPP sums inside
-// each row's lanes.  Any branch length is handled (no LDS).
+// each row's lanes.  No LDS; tokens past max_len are left untouched.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void branch_fwd_kernel(const T* __restrict__ qb,
                                                          const T* __restrict__ kb,
                                                          const T* __restrict__ vb, int nb,
                                                          const int32_t* __restrict__ bcu, int A,
-                                                         int bidir, int hq, int hkv,
+                                                         int max_len, int bidir, int hq, int hkv,
                                                          float scale_log2, float* o_acc,
                                                          float* lse_acc, int mode, T* o_out) {
   constexpr int LPR = D / 8;       // lanes per row
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(256) void branch_fwd_kernel(const T* __restrict__ q
   const int r = lane / LPR, col = 8 * (lane % LPR);
   const int t0 = max(0, min(bcu[a], nb));
   const int t1 = max(t0, min(bcu[a + 1], nb));
-  const int len = t1 - t0;
+  const int len = min(t1 - t0, max_len);   // tokens past the bound are left untouched
   for (int c0 = 0; c0 < G; c0 += RPW) {
     // lanes past the group's last q-head repeat its first and store nothing
     const bool row_ok = c0 + r < G;
@@ -213,83 +214,128 @@ __global__ __launch_bounds__(256) void branch_fwd_kernel(const T* __restrict__ q
 }
 
 // ---------------------------------------------------------------------------
-// Branch backward: one wave per (branch, kv-head).  For each row (t, h) and
-// each visible key u: s, P = exp2(s*c - lse2), dP = <dO, v_u>,
-// dS = P (dP - Delta); dq_row += dS k_u (registers), dk_u += dS q_row and
-// dv_u += P dO_row (LDS, lane-private slots, so no atomics).  The wave owns
-// every row and key it touches, so += on the global accumulators is race-free.
+// Branch backward: one wave per (branch, kv-head), rows laid out as in the
+// forward (D/8 lanes per row, 64/(D/8) q-heads per pass).  For a row (t, h)
+// and a visible key u: s = <q, k_u>, P = exp2(s*c - lse2), dP = <dO, v_u>,
+// dS = P (dP - Delta).  Two passes, both recomputing s and dP:
+//   1. token-outer: dq_row += dS k_u in registers, one += per row;
+//   2. key-outer: dk_u += dS q_row, dv_u += P dO_row in registers over every
+//      row that sees u, then summed over the pass's q-heads (shuffles across
+//      the row groups) and added once per key.
+// The wave owns every row and key it touches, so += on the global
+// accumulators is race-free and no LDS is needed.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(64) void branch_bwd_kernel(
+__global__ __launch_bounds__(256) void branch_bwd_kernel(
     const T* __restrict__ qb, const T* __restrict__ kb, const T* __restrict__ vb, int nb,
     const int32_t* __restrict__ bcu, int A, int max_len, int bidir, int hq, int hkv, float scale,
     const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     float* dq, float* dk, float* dv) {
-  constexpr int EPL = D / 64;
-  extern __shared__ float smem[];
-  float* dk_s = smem;                   // [max_len][D]
-  float* dv_s = smem + max_len * D;     // [max_len][D]
-  const int lane = threadIdx.x;
-  const int a = blockIdx.x;
+  constexpr int LPR = D / 8;       // lanes per row
+  constexpr int RPW = 64 / LPR;    // q-heads per pass
+  const int lane = threadIdx.x & 63;
+  const int a = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (a >= A) return;
   const int g = blockIdx.y;
   const int G = hq / hkv;
+  const int r = lane / LPR, col = 8 * (lane % LPR);
   const float scale_log2 = scale * kLog2e;
   const int t0 = max(0, min(bcu[a], nb));
   const int t1 = max(t0, min(bcu[a + 1], nb));
-  const int len = min(t1 - t0, max_len);
-  for (int u = 0; u < len; ++u)
+  const int len = min(t1 - t0, max_len);   // tokens past the bound are left untouched
+  // P and dS of row (t, h) and key u, given the row's q, dO, lse2, Delta
+  auto p_ds = [&](const float (&q)[8], const float (&d_o)[8], float lse2, float dl,
+                  const float (&kk)[8], const float (&vv)[8], float& p, float& ds) {
+    float s = 0.f, dp = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      dk_s[u * D + lane * EPL + e] = 0.f;
-      dv_s[u * D + lane * EPL + e] = 0.f;
+    for (int e = 0; e < 8; ++e) {
+      s = fmaf(q[e], kk[e], s);
+      dp = fmaf(d_o[e], vv[e], dp);
     }
-  for (int t = 0; t < len; ++t) {
-    const int kend = bidir ? len : t + 1;
-    for (int hl = 0; hl < G; ++hl) {
-      const int h = g * G + hl;
-      const size_t qoff = (static_cast<size_t>(t0 + t) * hq + h) * D;
+    s = group_sum<LPR>(s);
+    dp = group_sum<LPR>(dp);
+    p = (lse2 == kNegInf) ? 0.f : exp2_fast(s * scale_log2 - lse2);
+    ds = p * (dp - dl);
+  };
+  // pass 1: dQ
+  for (int c0 = 0; c0 < G; c0 += RPW) {
+    const bool row_ok = c0 + r < G;
+    const int h = g * G + (row_ok ? c0 + r : 0);
+    for (int t = 0; t < len; ++t) {
+      const int kend = bidir ? len : t + 1;
+      const size_t qoff = (static_cast<size_t>(t0 + t) * hq + h) * D + col;
       const size_t li = static_cast<size_t>(h) * nb + t0 + t;
-      float q[EPL], d_o[EPL], dqr[EPL];
-      load_lane<T, EPL>(qb, qoff, lane, q);
-      load_lane<T, EPL>(dout, qoff, lane, d_o);
+      float q[8], d_o[8], dqr[8];
+      load8<T>(qb, qoff, q);
+      load8<T>(dout, qoff, d_o);
+      const float lse2 = lse[li] * kLog2e, dl = delta[li];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) dqr[e] = 0.f;
-      const float lse2 = lse[li] * kLog2e;
-      const float dl = delta[li];
+      for (int e = 0; e < 8; ++e) dqr[e] = 0.f;
       for (int u = 0; u < kend; ++u) {
-        const size_t koff = (static_cast<size_t>(t0 + u) * hkv + g) * D;
-        float kk[EPL], vv[EPL];
-        load_lane<T, EPL>(kb, koff, lane, kk);
-        load_lane<T, EPL>(vb, koff, lane, vv);
-        float s = 0.f, dp = 0.f;
+        const size_t koff = (static_cast<size_t>(t0 + u) * hkv + g) * D + col;
+        float kk[8], vv[8], p, ds;
+        load8<T>(kb, koff, kk);
+        load8<T>(vb, koff, vv);
+        p_ds(q, d_o, lse2, dl, kk, vv, p, ds);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          s += q[e] * kk[e];
-          dp += d_o[e] * vv[e];
-        }
-        s = wave_sum(s);
-        dp = wave_sum(dp);
-        const float p = (lse2 == kNegInf) ? 0.f : exp2_fast(s * scale_log2 - lse2);
-        const float ds = p * (dp - dl);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          dqr[e] += ds * kk[e];
-          dk_s[u * D + lane * EPL + e] += ds * q[e];
-          dv_s[u * D + lane * EPL + e] += p * d_o[e];
-        }
+        for (int e = 0; e < 8; ++e) dqr[e] = fmaf(ds, kk[e], dqr[e]);
       }
+      if (!row_ok) continue;
+      float cur[8];
+      load8<float>(dq, qoff, cur);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) dq[qoff + lane * EPL + e] += scale * dqr[e];
+      for (int e = 0; e < 8; ++e) cur[e] = fmaf(scale, dqr[e], cur[e]);
+      store8<float>(dq, qoff, cur);
     }
   }
+  // pass 2: dK, dV
   for (int u = 0; u < len; ++u) {
-    const size_t koff = (static_cast<size_t>(t0 + u) * hkv + g) * D;
+    const size_t koff = (static_cast<size_t>(t0 + u) * hkv + g) * D + col;
+    float kk[8], vv[8], dka[8], dva[8];
+    load8<T>(kb, koff, kk);
+    load8<T>(vb, koff, vv);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      dk[koff + lane * EPL + e] += scale * dk_s[u * D + lane * EPL + e];
-      dv[koff + lane * EPL + e] += dv_s[u * D + lane * EPL + e];
+    for (int e = 0; e < 8; ++e) {
+      dka[e] = 0.f;
+      dva[e] = 0.f;
     }
+    for (int c0 = 0; c0 < G; c0 += RPW) {
+      const bool row_ok = c0 + r < G;
+      const int h = g * G + (row_ok ? c0 + r : 0);
+      for (int t = bidir ? 0 : u; t < len; ++t) {
+        const size_t qoff = (static_cast<size_t>(t0 + t) * hq + h) * D + col;
+        const size_t li = static_cast<size_t>(h) * nb + t0 + t;
+        float q[8], d_o[8], p, ds;
+        load8<T>(qb, qoff, q);
+        load8<T>(dout, qoff, d_o);
+        p_ds(q, d_o, lse[li] * kLog2e, delta[li], kk, vv, p, ds);
+        if (!row_ok) continue;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          dka[e] = fmaf(ds, q[e], dka[e]);
+          dva[e] = fmaf(p, d_o[e], dva[e]);
+        }
+      }
+    }
+    // sum over the row groups (lanes that differ by multiples of LPR)
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dka[e] += __shfl_xor(dka[e], off);
+        dva[e] += __shfl_xor(dva[e], off);
+      }
+    if (r != 0) continue;
+    float ck[8], cv[8];
+    load8<float>(dk, koff, ck);
+    load8<float>(dv, koff, cv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ck[e] = fmaf(scale, dka[e], ck[e]);
+      cv[e] += dva[e];
+    }
+    store8<float>(dk, koff, ck);
+    store8<float>(dv, koff, cv);
   }
 }
 
@@ -298,8 +344,9 @@ static void branch_fwd_d(const BranchArgs& a) {
   const dim3 grid((a.num_branches + 3) / 4, a.hkv);
   hipLaunchKernelGGL((branch_fwd_kernel<T, D>), grid, dim3(256), 0, a.stream,
                      static_cast<const T*>(a.qb), static_cast<const T*>(a.kb),
-                     static_cast<const T*>(a.vb), a.nb, a.branch_cu, a.num_branches, a.bidir, a.hq,
-                     a.hkv, a.scale * kLog2e, a.o_acc, a.lse_acc, a.mode, static_cast<T*>(a.o_out));
+                     static_cast<const T*>(a.vb), a.nb, a.branch_cu, a.num_branches, a.max_len,
+                     a.bidir, a.hq, a.hkv, a.scale * kLog2e, a.o_acc, a.lse_acc, a.mode,
+                     static_cast<T*>(a.o_out));
 }
 
 hipError_t launch_branch_fwd(const BranchArgs& a) {
@@ -314,9 +361,8 @@ hipError_t launch_branch_fwd(const BranchArgs& a) {
 
 template <typename T, int D>
 static void branch_bwd_d(const BranchArgs& a) {
-  const dim3 grid(a.num_branches, a.hkv);
-  const size_t lds = branch_bwd_lds_bytes(a.max_len, D);
-  hipLaunchKernelGGL((branch_bwd_kernel<T, D>), grid, dim3(64), lds, a.stream,
+  const dim3 grid((a.num_branches + 3) / 4, a.hkv);
+  hipLaunchKernelGGL((branch_bwd_kernel<T, D>), grid, dim3(256), 0, a.stream,
                      static_cast<const T*>(a.qb), static_cast<const T*>(a.kb),
                      static_cast<const T*>(a.vb), a.nb, a.branch_cu, a.num_branches, a.max_len,
                      a.bidir, a.hq, a.hkv, a.scale, static_cast<const T*>(a.dout), a.lse, a.delta,
