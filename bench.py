@@ -291,7 +291,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="eagle3_256k")
-    ap.add_argument("--cpu-anchors", type=int, default=12,
+    ap.add_argument("--cpu-anchors", type=int, default=16,
                     help="anchors whose rows the CPU oracle processes for cpu_baseline (0: skip)")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")

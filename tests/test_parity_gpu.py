@@ -197,3 +197,50 @@ def test_check_index_counts_violations():
     pos = torch.tensor([0, 1, 1, 0, -3, 5], dtype=torch.int32, device="cuda")
     assert attn_check_index(seq, pos, strict=False) == 2   # (1,-3): pos<0 and order; (0,5)<(1,-3)
     assert attn_check_index(seq, pos, strict=True) == 3    # plus the repeated (0,1)
+
+
+@pytest.mark.parametrize("kind,d", [("causal", 128), ("bidir", 64)])
+def test_branch_tokens_past_max_len_are_left_untouched(kind, d):
+    """Branches of 6 tokens called with max_branch_len = 4 (a precondition
+    violation the header defines): tokens 4 and 5 keep the buffers' previous
+    contents, and tokens 0..3 get exactly what a call on the branches cut to
+    their first 4 tokens gives (same kernel arithmetic, so bit-exact)."""
+    from branch_aware_causal_amd import api
+    say(f"case branch max_len clamp: kind={kind} d={d}")
+    dev = torch.device("cuda:0")
+    A, L, B, hq, hkv = 37, 6, 4, 8, 2
+    nb = A * L
+    gen = torch.Generator(device=dev).manual_seed(2024 + d)
+    rnd = lambda *s: torch.randn(*s, generator=gen, device=dev).to(torch.bfloat16)
+    qb, dob = rnd(nb, hq, d), rnd(nb, hq, d)
+    kb, vb = rnd(nb, hkv, d), rnd(nb, hkv, d)
+    cu = torch.arange(0, nb + 1, L, dtype=torch.int32, device=dev)
+    idx = torch.tensor([a * L + t for a in range(A) for t in range(B)], device=dev)
+    rest = torch.tensor([a * L + t for a in range(A) for t in range(B, L)], device=dev)
+    cu_c = torch.arange(0, A * B + 1, B, dtype=torch.int32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    # forward
+    o = torch.full((nb, hq, d), 7.0, **f32)
+    lse = torch.full((hq, nb), 7.0, **f32)
+    api.attn_branch_fwd(qb, kb, vb, cu, B, kind, o, lse, "write")
+    o_c, lse_c = torch.empty(A * B, hq, d, **f32), torch.empty(hq, A * B, **f32)
+    api.attn_branch_fwd(qb[idx].contiguous(), kb[idx].contiguous(), vb[idx].contiguous(), cu_c, B,
+                        kind, o_c, lse_c, "write")
+    torch.cuda.synchronize()
+    assert torch.equal(o[idx], o_c) and torch.equal(lse[:, idx], lse_c)
+    assert bool((o[rest] == 7.0).all()) and bool((lse[:, rest] == 7.0).all())
+    # backward
+    delta = torch.randn(hq, nb, generator=gen, device=dev)
+    lse_in = lse.clone()
+    lse_in[:, rest] = 0.0
+    grads = [torch.zeros(nb, hq, d, **f32), torch.zeros(nb, hkv, d, **f32), torch.zeros(nb, hkv, d, **f32)]
+    api.attn_branch_bwd(qb, kb, vb, cu, B, kind, dob, lse_in, delta, *grads)
+    grads_c = [torch.zeros(A * B, hq, d, **f32), torch.zeros(A * B, hkv, d, **f32),
+               torch.zeros(A * B, hkv, d, **f32)]
+    api.attn_branch_bwd(qb[idx].contiguous(), kb[idx].contiguous(), vb[idx].contiguous(), cu_c, B,
+                        kind, dob[idx].contiguous(), lse_c, delta[:, idx].contiguous(), *grads_c)
+    torch.cuda.synchronize()
+    for full, comp in zip(grads, grads_c):
+        assert torch.equal(full[idx], comp)
+        assert bool((full[rest] == 0.0).all())
+        assert bool(torch.isfinite(comp).all()) and float(comp.abs().max()) > 0
