@@ -339,6 +339,112 @@ __global__ __launch_bounds__(256) void branch_bwd_kernel(
   }
 }
 
+// Branch backward for branches of at most MAXL tokens (used with MAXL = 4): one
+// token-outer pass in the same row layout, with dK/dV of every key of the
+// branch in registers (dQ accumulates per row as in the two-pass kernel), so
+// each row's Q and dO are read once.  The keys' sums over the group's
+// q-heads are taken at the end.
+template <typename T, int D, int MAXL>
+__global__ __launch_bounds__(256) void branch_bwd_short_kernel(
+    const T* __restrict__ qb, const T* __restrict__ kb, const T* __restrict__ vb, int nb,
+    const int32_t* __restrict__ bcu, int A, int max_len, int bidir, int hq, int hkv, float scale,
+    const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    float* dq, float* dk, float* dv) {
+  constexpr int LPR = D / 8;       // lanes per row
+  constexpr int RPW = 64 / LPR;    // q-heads per pass
+  const int lane = threadIdx.x & 63;
+  const int a = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (a >= A) return;
+  const int g = blockIdx.y;
+  const int G = hq / hkv;
+  const int r = lane / LPR, col = 8 * (lane % LPR);
+  const float scale_log2 = scale * kLog2e;
+  const int t0 = max(0, min(bcu[a], nb));
+  const int t1 = max(t0, min(bcu[a + 1], nb));
+  const int len = min(min(t1 - t0, max_len), MAXL);   // tokens past the bound are left untouched
+  float dka[MAXL][8], dva[MAXL][8];
+#pragma unroll
+  for (int u = 0; u < MAXL; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      dka[u][e] = 0.f;
+      dva[u][e] = 0.f;
+    }
+  for (int c0 = 0; c0 < G; c0 += RPW) {
+    const bool row_ok = c0 + r < G;
+    const int h = g * G + (row_ok ? c0 + r : 0);
+    const float keep_row = row_ok ? 1.f : 0.f;
+#pragma unroll
+    for (int t = 0; t < MAXL; ++t) {
+      if (t >= len) break;
+      const int kend = bidir ? len : t + 1;
+      const size_t qoff = (static_cast<size_t>(t0 + t) * hq + h) * D + col;
+      const size_t li = static_cast<size_t>(h) * nb + t0 + t;
+      float q[8], d_o[8], dqr[8];
+      load8<T>(qb, qoff, q);
+      load8<T>(dout, qoff, d_o);
+      const float lse2 = lse[li] * kLog2e, dl = delta[li];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dqr[e] = 0.f;
+#pragma unroll
+      for (int u = 0; u < MAXL; ++u) {
+        if (u >= kend) break;
+        const size_t koff = (static_cast<size_t>(t0 + u) * hkv + g) * D + col;
+        float kk[8], vv[8];
+        load8<T>(kb, koff, kk);
+        load8<T>(vb, koff, vv);
+        float sc = 0.f, dp = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          sc = fmaf(q[e], kk[e], sc);
+          dp = fmaf(d_o[e], vv[e], dp);
+        }
+        sc = group_sum<LPR>(sc);
+        dp = group_sum<LPR>(dp);
+        const float p = (lse2 == kNegInf) ? 0.f : exp2_fast(sc * scale_log2 - lse2);
+        const float ds = p * (dp - dl);
+        const float dsk = ds * keep_row, pk = p * keep_row;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          dqr[e] = fmaf(ds, kk[e], dqr[e]);
+          dka[u][e] = fmaf(dsk, q[e], dka[u][e]);
+          dva[u][e] = fmaf(pk, d_o[e], dva[u][e]);
+        }
+      }
+      if (!row_ok) continue;
+      float cur[8];
+      load8<float>(dq, qoff, cur);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cur[e] = fmaf(scale, dqr[e], cur[e]);
+      store8<float>(dq, qoff, cur);
+    }
+  }
+  // dK/dV: sum over the row groups (lanes that differ by multiples of LPR)
+#pragma unroll
+  for (int u = 0; u < MAXL; ++u) {
+    if (u >= len) break;
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dka[u][e] += __shfl_xor(dka[u][e], off);
+        dva[u][e] += __shfl_xor(dva[u][e], off);
+      }
+    if (r != 0) continue;
+    const size_t koff = (static_cast<size_t>(t0 + u) * hkv + g) * D + col;
+    float ck[8], cv[8];
+    load8<float>(dk, koff, ck);
+    load8<float>(dv, koff, cv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ck[e] = fmaf(scale, dka[u][e], ck[e]);
+      cv[e] += dva[u][e];
+    }
+    store8<float>(dk, koff, ck);
+    store8<float>(dv, koff, cv);
+  }
+}
+
 template <typename T, int D>
 static void branch_fwd_d(const BranchArgs& a) {
   const dim3 grid((a.num_branches + 3) / 4, a.hkv);
@@ -362,6 +468,16 @@ hipError_t launch_branch_fwd(const BranchArgs& a) {
 template <typename T, int D>
 static void branch_bwd_d(const BranchArgs& a) {
   const dim3 grid((a.num_branches + 3) / 4, a.hkv);
+  if (a.max_len <= 4) {
+    // every key's dK/dV in registers: one pass.  (For 8-token branches the
+    // registers this takes cut occupancy below what the second pass costs.)
+    hipLaunchKernelGGL((branch_bwd_short_kernel<T, D, 4>), grid, dim3(256), 0, a.stream,
+                       static_cast<const T*>(a.qb), static_cast<const T*>(a.kb),
+                       static_cast<const T*>(a.vb), a.nb, a.branch_cu, a.num_branches, a.max_len,
+                       a.bidir, a.hq, a.hkv, a.scale, static_cast<const T*>(a.dout), a.lse,
+                       a.delta, a.dq, a.dk, a.dv);
+    return;
+  }
   hipLaunchKernelGGL((branch_bwd_kernel<T, D>), grid, dim3(256), 0, a.stream,
                      static_cast<const T*>(a.qb), static_cast<const T*>(a.kb),
                      static_cast<const T*>(a.vb), a.nb, a.branch_cu, a.num_branches, a.max_len,
