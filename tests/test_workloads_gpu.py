@@ -193,9 +193,12 @@ def test_256k_full_size():
     v_host = t["v"].float().cpu().numpy()
     prob.k, prob.v = k_host, v_host
     N = st.n_main
-    A = np.concatenate([np.arange(4), np.arange(N - 4, N),
-                        np.random.default_rng(3).choice(N, size=8, replace=False)])
-    A = np.unique(A)
+    # 64 anchors: the first and last 8, and one in each of 48 equal position
+    # bins (seeded), so that every stretch of the sequence is sampled
+    rng = np.random.default_rng(3)
+    edges = np.linspace(8, N - 8, 49).astype(np.int64)
+    strat = np.array([rng.integers(edges[i], edges[i + 1]) for i in range(48)])
+    A = np.unique(np.concatenate([np.arange(8), np.arange(N - 8, N), strat]))
     br = np.concatenate([np.arange(st.branch_cu[a], st.branch_cu[a + 1]) for a in A])
     check_rows(prob, gpu, t, A.astype(np.int64), br, w.name)
     # dK/dV of the last 128 positions (and their branches), kv-head 0
