@@ -169,14 +169,19 @@ def test_block_branch_workloads(name):
     check_rne(gpu)
     check_invariants(gpu, t, w.name)
     prob = problem(st, t, lazy=True)
-    m, b = sample_anchor_rows(st, 10, np.random.default_rng(1))
+    m, b = sample_anchor_rows(st, 40, np.random.default_rng(1))
     # plus main rows between anchors
-    extra = np.random.default_rng(2).choice(st.n_main, size=6, replace=False)
+    extra = np.random.default_rng(2).choice(st.n_main, size=16, replace=False)
     check_rows(prob, gpu, t, np.unique(np.concatenate([m, extra])), b, w.name)
     cu = st.cu_seqlens.astype(np.int64)
     last_anchor = st.n_branches - 1
     bk = np.arange(st.branch_cu[last_anchor], st.branch_cu[last_anchor + 1])
-    check_key_columns(prob, gpu, t, cu[1:] - 1, bk, w.name)
+    # key columns: the last key of every sequence and one key in each of 32
+    # equal bins of the packed main tokens (seeded)
+    rng = np.random.default_rng(4)
+    edges = np.linspace(0, st.n_main, 33).astype(np.int64)
+    strat = np.array([rng.integers(edges[i], edges[i + 1]) for i in range(32)])
+    check_key_columns(prob, gpu, t, np.unique(np.concatenate([cu[1:] - 1, strat])), bk, w.name)
 
 
 @pytest.mark.timeout(900)
@@ -265,5 +270,9 @@ def test_256k_rank0_share_of_zigzag_8():
     prob.v = t["v"].float().cpu().numpy()
     N = st.n_main
     A = np.array([0, 1, 16383, 15 * 16384, 15 * 16384 + 1, N - 1, 9000, 250000])
+    # and 12 seeded anchors in each of the rank's two query chunks
+    rng = np.random.default_rng(5)
+    A = np.unique(np.concatenate([A, rng.integers(0, 16384, 12),
+                                  rng.integers(15 * 16384, 16 * 16384, 12)]))
     br = np.concatenate([np.arange(st.branch_cu[a], st.branch_cu[a + 1]) for a in A])
     check_rows(prob, gpu, t, A.astype(np.int64), br, w.name)
