@@ -140,6 +140,50 @@ def test_varlen_20k_full_size():
     check_key_columns(prob, gpu, t, mk, bk, w.name)
 
 
+@pytest.mark.timeout(900)
+def test_varlen_20k_one_kv_group_in_full():
+    """Every row and every key of the 20K varlen workload against the oracle
+    in definition mode (one masked softmax per row over its main prefix and
+    its own branch), restricted to kv-head 0 and its q-heads: O, lse and dQ of
+    all rows, dK and dV of all main and branch keys."""
+    from oracle.attention import _blocks, delta, grads, partial
+    w = WORKLOADS["eagle3_varlen_20k"]
+    st, t = inputs(w)
+    gpu = run_path(st, t)
+    prob = problem(st, t, lazy=True)
+    G = w.hq // w.hkv
+    heads = list(range(G))
+    N, n = st.n_main, st.n_main + st.n_branch_tok
+    O = np.zeros((n, G, w.d))
+    lse = np.full((n, G), -np.inf)
+    dQ = np.zeros((n, G, w.d))
+    dK = np.zeros((n, w.d))
+    dV = np.zeros((n, w.d))
+    dev = t["do"].device
+    for rows, keys in _blocks(prob, 128):
+        o, l = partial(prob, rows, keys, heads)
+        dO = np.zeros((rows.size, w.hq, w.d))
+        m = rows < N
+        dO[m, :G] = host64(t["do"][torch.as_tensor(rows[m], device=dev)][:, :G])
+        dO[~m, :G] = host64(t["dob"][torch.as_tensor(rows[~m] - N, device=dev)][:, :G])
+        dq, dk, dv = grads(prob, rows, keys, l, dO, delta(o, dO), heads)
+        O[rows], lse[rows] = o[:, :G], l[:, :G]
+        dQ[rows] += dq[:, :G]
+        dK[keys] += dk[:, 0]
+        dV[keys] += dv[:, 0]
+    g_o = np.concatenate([host64(gpu["o_main_acc"][:, :G]), host64(gpu["o_br_acc"][:, :G])])
+    g_l = np.concatenate([host64(gpu["lse_main"][:G]).T, host64(gpu["lse_br"][:G]).T])
+    g_q = np.concatenate([host64(gpu["dq_main"][:, :G]), host64(gpu["dq_br"][:, :G])])
+    g_k = np.concatenate([host64(gpu["dk"][:, 0]), host64(gpu["dkb"][:, 0])])
+    g_v = np.concatenate([host64(gpu["dv"][:, 0]), host64(gpu["dvb"][:, 0])])
+    e = dict(o=maxdiff(g_o, O), lse=maxdiff(g_l, lse), dq=maxdiff(g_q, dQ), dk=maxdiff(g_k, dK),
+             dv=maxdiff(g_v, dV))
+    say(f"[{w.name}] all {n} rows x {G} heads, all {n} keys of kv-head 0: " +
+        ", ".join(f"{k}={v:.2e}" for k, v in e.items()))
+    assert e["o"] <= TOL_O and e["lse"] <= TOL_L, e
+    assert e["dq"] <= TOL_G and e["dk"] <= TOL_G and e["dv"] <= TOL_G, e
+
+
 @pytest.mark.parametrize("cp", [2, 4, 8])
 def test_varlen_20k_zigzag_ring(cp):
     w = WORKLOADS["eagle3_varlen_20k"]
