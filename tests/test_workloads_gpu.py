@@ -141,13 +141,14 @@ def test_varlen_20k_full_size():
 
 
 @pytest.mark.timeout(900)
-def test_varlen_20k_one_kv_group_in_full():
-    """Every row and every key of the 20K varlen workload against the oracle
-    in definition mode (one masked softmax per row over its main prefix and
-    its own branch), restricted to kv-head 0 and its q-heads: O, lse and dQ of
+@pytest.mark.parametrize("name", ["eagle3_varlen_20k", "dflash_32k", "dspark_4x16k"])
+def test_one_kv_group_in_full(name):
+    """Every row and every key of the workload against the oracle in
+    definition mode (one masked softmax per row over its main prefix and its
+    own branch), restricted to kv-head 0 and its q-heads: O, lse and dQ of
     all rows, dK and dV of all main and branch keys."""
     from oracle.attention import _blocks, delta, grads, partial
-    w = WORKLOADS["eagle3_varlen_20k"]
+    w = WORKLOADS[name]
     st, t = inputs(w)
     gpu = run_path(st, t)
     prob = problem(st, t, lazy=True)
