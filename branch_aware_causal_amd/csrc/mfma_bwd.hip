@@ -50,6 +50,10 @@ constexpr int NW = 8;
 //     read in half-steps 2t .. 2t+3, V(t) in 2t and 2t+1.  Team 0 loads
 //     K(t+1) and V(t+1) at the start of half-step 2t and waits for them
 //     before the barrier that ends half-step 2t+1.
+//   * A wave reads the first K^T operands of its next MFMA stream at the end
+//     of its GRAD half-step (it has slack there), and runs its MFMA streams
+//     at raised issue priority so that the partner's vector work yields to
+//     them on the shared SIMD.
 template <int D, int G>
 __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ q_seq,
@@ -174,9 +178,20 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
   // dP^T = V dO^T for this tile (4*KS MFMAs, alternating).  LDS operands are
   // read kPre MFMAs ahead.
   constexpr int kPre = 2;
+  // the first kPre operands of a stream that starts with dQ are read at the
+  // end of the wave's previous GRAD half-step (pre_dq), off the MFMA path
+  bf16x8 opa[kPre];
+  auto pre_dq = [&](const uint16_t* kprev) {
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+      const int kb = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
+      opa[j] = tr_operand<D>(kprev, lo_off, kb * 32 + 16 * s2, mb);
+    }
+  };
   auto mfma_stream = [&](auto dq_c, auto s_c, const uint16_t* kprev, const uint16_t* kt,
                          const uint16_t* vt) {
     constexpr bool kDQ = decltype(dq_c)::value, kS = decltype(s_c)::value;
+    __builtin_amdgcn_s_setprio(1);
     constexpr int NP = kDQ ? 4 * MB : 0, N = NP + (kS ? 4 * KS : 0);
     // step j >= NP: i = j - NP; S (even i) / dP (odd i) of block kb, k-step ks
     auto load_a = [&](int j) {
@@ -187,10 +202,9 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
       const int i = j - NP, kb = (i / 2) % 2, ks = i / 4;
       return row_operand<D>((i & 1) ? vt : kt, lo_off, kb * 32, ks);
     };
-    bf16x8 opa[kPre];
+    if constexpr (!kDQ) {
 #pragma unroll
-    for (int j = 0; j < kPre; ++j) {
-      opa[j] = load_a(j);
+      for (int j = 0; j < kPre; ++j) opa[j] = load_a(j);
     }
     if (kS) {
 #pragma unroll
@@ -215,14 +229,11 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
         opa[j % kPre] = load_a(j + kPre);
       }
     }
-    // pin the order: the first kPre steps' operands, then one MFMA and the
-    // operand of the step kPre ahead (2 LDS reads for a dQ step, 1 for S / dP)
+    // pin the order: (without dQ) the first kPre operands, then one MFMA and
+    // the operand of the step kPre ahead (2 LDS reads for a dQ step, 1 for S / dP)
     static_assert(NP == 0 || NP >= kPre, "prefetch covers one operand kind");
     static_assert(kPre % 2 == 0, "S / dP alternate");
-    if constexpr (NP > 0)
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre, 0);
-    else
-      __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+    if constexpr (NP == 0) __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
 #pragma unroll
     for (int j = 0; j < N; ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -238,7 +249,7 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
     for (int kb = 0; kb < 2; ++kb) {
       keep(sacc[kb]);
       keep(dpacc[kb]);
-    }
+    }    __builtin_amdgcn_s_setprio(0);
   };
 
   // GRAD half-step of the tile at j0: dS (bf16) into db; a tile this wave
@@ -286,6 +297,7 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
     if (do_s) mfma_stream(BoolC<false>(), BoolC<true>(), &Ks[2][0], &Ks[0][0], &Vs[0][0]);
     wg_barrier<kWaitNone>();
     grad(lo, do_s);
+    pre_dq(&Ks[0][0]);
     any_prev = do_s;
     wg_barrier<kWaitAll>();     // team 0's loads of this tile pair have landed
   }
@@ -303,6 +315,7 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
       mfma_stream(BoolC<true>(), BoolC<true>(), &Ks[cp][0], &Ks[c][0], &Vs[t & 1][0]);
     wg_barrier<kWaitNone>();
     grad(j0, do_s);
+    pre_dq(&Ks[c][0]);
     any_prev = do_s;
     wg_barrier<kWaitAll>();
     c = cn;
