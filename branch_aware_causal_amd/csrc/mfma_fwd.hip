@@ -19,7 +19,8 @@
 //     interval, also found by binary search, so masks are index compares.
 //   * Ping-pong: waves w and w+4 share a SIMD and run one half-step apart
 //     (barrier between half-steps), so that while one issues the tile's 32
-//     MFMAs the other runs its softmax on the vector ALUs.
+//     MFMAs the other runs its softmax on the vector ALUs.  The MFMA stream
+//     runs at raised wave priority, so the partner's vector work yields to it.
 //   * Scores are computed transposed, S^T = K Q^T (keys x rows), so each lane
 //     holds 32 scores of ONE query row: the row max is in-lane plus one
 //     exchange with lane n+32, and the row sums stay per lane until the end.
@@ -194,6 +195,7 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
     constexpr bool kPV = decltype(pv_c)::value, kS = decltype(s_c)::value;
     constexpr bool kDMA = decltype(dma_c)::value;
     constexpr int NP = kPV ? 4 * MB : 0, N = NP + (kS ? 2 * KS : 0);
+    __builtin_amdgcn_s_setprio(1);
     constexpr int kGap = N / (2 * ROUNDS);
     static_assert(!kDMA || kGap >= 1, "load rounds fit in the stream");
     auto load = [&](int j) {
@@ -248,7 +250,7 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) keep(oacc[mb]);
     keep(sacc[0]);
-    keep(sacc[1]);
+    keep(sacc[1]);    __builtin_amdgcn_s_setprio(0);
   };
 
   // softmax half-step of the tile at j0: scores -> P (bf16) in pb; a tile
