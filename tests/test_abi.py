@@ -167,3 +167,17 @@ def test_plan_rejects_malformed_inputs(args, needle):
     with pytest.raises(BacError) as ei:
         zigzag_shard_plan(cu, bcu, anchor, args.get("cp", 2), args.get("rank", 0))
     assert ei.value.status == -1 and needle in ei.value.message
+
+
+def test_plan_matches_hand_computed_fixtures():
+    """The C++ plan against the hand-computed fixtures of tests/golden
+    (floor chunk split where 2C does not divide the length, an empty
+    sequence, branch ownership, ring order)."""
+    from test_oracle import PLAN_FILES, PLAN_KEYS, load_plan_golden
+    from branch_aware_causal_amd import zigzag_shard_plan
+    for fname in PLAN_FILES:
+        cu, bcu, anchors, C_, _, ranks = load_plan_golden(fname)
+        for r, want in ranks.items():
+            got = zigzag_shard_plan(cu, bcu, anchors, C_, r)
+            for key in PLAN_KEYS:
+                assert np.array_equal(got[key], want[key].astype(np.int32)), (fname, r, key)

@@ -486,3 +486,45 @@ def test_varlen_lengths_seed0():
     lens = varlen_lengths(20480, 512, 8192, 0)
     assert sum(lens) == 20480 and all(512 <= L <= 8192 for L in lens[:-1])
     assert lens == (4573, 1522, 1382, 1818, 7909, 3276)
+
+
+# ---------------------------------------------------------------------------
+# Zigzag plan against hand-computed fixtures (chunk split, ownership, ring
+# order and received bytes where 2C does not divide the length)
+# ---------------------------------------------------------------------------
+
+PLAN_FILES = sorted(f for f in os.listdir(GOLDEN) if f.startswith("plan_"))
+PLAN_KEYS = ("main_index", "main_seq", "main_pos", "branch_ids", "branch_index", "branch_seq",
+             "branch_pos", "branch_t", "local_branch_cu", "kv_src")
+
+
+def load_plan_golden(name):
+    """Returns (cu_seqlens, branch_cu, anchors, C, bytes_params, {rank: {key: array}})."""
+    head, ranks, cur = {}, {}, None
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, *vals = line.split()
+            vals = [int(v) for v in vals]
+            if key == "rank":
+                cur = ranks.setdefault(vals[0], {})
+            elif cur is None:
+                head[key] = vals
+            else:
+                cur[key] = np.asarray(vals, dtype=np.int64)
+    cu = np.concatenate([[0], np.cumsum(head["seqlens"])]).astype(np.int64)
+    bcu = np.concatenate([[0], np.cumsum(head["branch_lens"])]).astype(np.int64)
+    return cu, bcu, np.asarray(head["anchors"], np.int64), head["C"][0], head["bytes_params"], ranks
+
+
+@pytest.mark.parametrize("fname", PLAN_FILES)
+def test_zigzag_plan_matches_hand_computed_fixture(fname):
+    cu, bcu, anchors, C, (hkv, d, eb), ranks = load_plan_golden(fname)
+    assert sorted(ranks) == list(range(C))
+    for r, want in ranks.items():
+        got = zigzag.plan(cu, bcu, anchors, C, r)
+        for key in PLAN_KEYS:
+            assert np.array_equal(got[key], want[key]), (fname, r, key, got[key], want[key])
+        assert zigzag.ring_bytes_received(cu, bcu, anchors, C, r, hkv, d, eb) == want["ring_bytes"][0]
