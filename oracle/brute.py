@@ -14,6 +14,11 @@ from __future__ import annotations
 import math
 
 
+def _kind_of(kind, a):
+    """Kind of branch a: one kind for every branch, or one per branch."""
+    return kind if isinstance(kind, str) else kind[a]
+
+
 def _row_keys(cu, bcu, anchor, kind, row):
     """Visible keys of a row as ('m', global_idx) / ('b', branch_token_idx)."""
     S = len(cu) - 1
@@ -35,7 +40,7 @@ def _row_keys(cu, bcu, anchor, kind, row):
             keys.append(("m", cu[s] + kpos))
         blen = bcu[a + 1] - bcu[a]
         for u in range(blen):
-            if kind == "bidir" or u <= t:
+            if _kind_of(kind, a) == "bidir" or u <= t:
                 keys.append(("b", bcu[a] + u))
     return keys
 

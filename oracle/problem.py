@@ -12,7 +12,9 @@ blocks):
 * branch row (a, t), anchored at main position (s_a, j_a), sees main keys
   (s_a, k) with k <= j_a, plus keys (a, u) of its own branch with u <= t for
   causal kinds (EAGLE-3 TTT, DSpark) or every u for the bidirectional kind
-  (DFlash).  It never sees another branch's keys.
+  (DFlash).  It never sees another branch's keys.  Each branch carries its
+  own kind, so one packed batch may mix the three draft families ([G] 技术贡献:
+  one design serves EAGLE-3, DFlash and DSpark).
 
 Readings where the pages are silent: the anchor itself is part of the visible
 prefix; a branch token sees itself; sequences packed together never see each
@@ -36,6 +38,8 @@ class Problem:
 
     Tensor arguments may be numpy arrays or any object whose ``[index_array]``
     returns rows as an array (values are upcast to fp64 on access).
+    ``kind`` is "causal" or "bidir" for every branch, or a sequence with one
+    of them per branch.
     """
 
     def __init__(self, cu_seqlens, branch_cu, branch_anchor, kind, hq, hkv, d,
@@ -43,7 +47,6 @@ class Problem:
         self.cu = np.asarray(cu_seqlens, dtype=np.int64)
         self.bcu = np.asarray(branch_cu, dtype=np.int64)
         self.anchor = np.asarray(branch_anchor, dtype=np.int64)
-        assert kind in ("causal", "bidir")
         self.kind = kind
         self.hq, self.hkv, self.d = int(hq), int(hkv), int(d)
         assert self.hq % self.hkv == 0
@@ -60,6 +63,13 @@ class Problem:
         # per branch token: branch id and index t inside the branch
         self.branch_of_tok = np.repeat(np.arange(self.A, dtype=np.int64), np.diff(self.bcu))
         self.t_of_tok = np.arange(self.Nb, dtype=np.int64) - self.bcu[self.branch_of_tok]
+        if isinstance(kind, str):
+            assert kind in ("causal", "bidir")
+            kinds = [kind] * self.A
+        else:
+            kinds = list(kind)
+            assert len(kinds) == self.A and all(k in ("causal", "bidir") for k in kinds)
+        self.bidir_of_branch = np.asarray([k == "bidir" for k in kinds], dtype=bool)
         self.anchor_seq = self.seq_of_main[self.anchor] if self.A else np.zeros(0, np.int64)
         self.anchor_pos = self.pos_of_main[self.anchor] if self.A else np.zeros(0, np.int64)
         self.group = np.arange(self.hq) * self.hkv // self.hq   # kv-head of each q-head
@@ -85,8 +95,8 @@ class Problem:
         kb, ks, kp, kbr, kt = self.describe(keys)
         main_vis = (~kb)[None, :] & (ks[None, :] == rs[:, None]) & (kp[None, :] <= rp[:, None])
         same = kb[None, :] & rb[:, None] & (kbr[None, :] == rbr[:, None])
-        if self.kind == "causal":
-            same &= kt[None, :] <= rt[:, None]
+        bidir = self.bidir_of_branch[np.maximum(rbr, 0)] if self.A else np.zeros(rbr.shape, bool)
+        same &= (kt[None, :] <= rt[:, None]) | (rb & bidir)[:, None]
         return main_vis | same
 
     def visible_keys(self, rows):

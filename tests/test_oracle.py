@@ -50,6 +50,19 @@ def dspark(seqlens, B, stride, **kw):
     return rand_problem(seqlens, an, [B] * sum(len(a) for a in an), "causal", **kw)
 
 
+def kind_of(prob, a):
+    """Kind of branch a as given to the problem (one for all, or per branch)."""
+    return prob.kind if isinstance(prob.kind, str) else prob.kind[a]
+
+
+# one packed batch of the three families: an EAGLE-3 depth-2 chain at every
+# position of a 6-token sequence, DFlash blocks of 4 every 4 positions of an
+# 8-token sequence, DSpark blocks of 3 every 2 positions of a 5-token one
+MIXED = dict(seqlens=(6, 8, 5), anchors=[list(range(6)), [0, 4], [0, 2, 4]],
+             lens=[2] * 6 + [4, 4] + [3, 3, 3],
+             kinds=["causal"] * 6 + ["bidir"] * 2 + ["causal"] * 3)
+
+
 SMALL_CASES = {
     "eagle_d3": lambda **kw: eagle((5, 7), 3, **kw),
     "dflash_b4": lambda **kw: dflash((8, 6), 4, 4, **kw),
@@ -57,6 +70,8 @@ SMALL_CASES = {
     "ragged": lambda **kw: rand_problem((1, 6, 3), [[0], [0, 2, 5], [1]], [2, 1, 4, 3, 2],
                                         "causal", **kw),
     "ragged_bidir": lambda **kw: rand_problem((4, 5), [[3], [0, 4]], [3, 1, 5], "bidir", **kw),
+    "mixed_kinds": lambda **kw: rand_problem(MIXED["seqlens"], MIXED["anchors"], MIXED["lens"],
+                                             MIXED["kinds"], **kw),
 }
 
 
@@ -92,7 +107,8 @@ def golden_problem(spec, d=4):
     blens = [int(x) for x in spec["branch_lens"]]
     cu = np.concatenate([[0], np.cumsum(seqlens)])
     per_seq = [[a - cu[s] for a in anchors if cu[s] <= a < cu[s + 1]] for s in range(len(seqlens))]
-    return rand_problem(seqlens, per_seq, blens, spec["kind"][0], hq=2, hkv=1, d=d)
+    kind = spec["kinds"] if "kinds" in spec else spec["kind"][0]
+    return rand_problem(seqlens, per_seq, blens, kind, hq=2, hkv=1, d=d)
 
 
 @pytest.mark.parametrize("fname", GOLDEN_FILES)
@@ -143,7 +159,7 @@ def closed_form_count(prob, row):
     j = int(ag - prob.cu[s])
     blen = int(prob.bcu[a + 1] - prob.bcu[a])
     t = int(bt - prob.bcu[a])
-    return j + 1 + (t + 1 if prob.kind == "causal" else blen)
+    return j + 1 + (t + 1 if kind_of(prob, a) == "causal" else blen)
 
 
 @pytest.mark.parametrize("case", sorted(SMALL_CASES))
@@ -166,7 +182,7 @@ def test_q_zero_closed_form(case):
             a = np.searchsorted(prob.bcu, bt, side="right") - 1
             ag = prob.anchor[a]
             s = np.searchsorted(prob.cu, ag, side="right") - 1
-            last = bt + 1 if prob.kind == "causal" else prob.bcu[a + 1]
+            last = bt + 1 if kind_of(prob, a) == "causal" else prob.bcu[a + 1]
             vrows = np.concatenate([prob.v[prob.cu[s]:ag + 1], prob.vb[prob.bcu[a]:last]])
         assert vrows.shape[0] == n
         mean = vrows.mean(axis=0)                       # [Hkv, d]
@@ -282,6 +298,7 @@ ZZ_CASES = [
     ("eagle", lambda: eagle((9, 16, 3), 2, hq=4, hkv=2, d=4, seed=2)),
     ("dflash", lambda: dflash((16, 11), 4, 4, hq=2, hkv=1, d=4, seed=3)),
     ("dspark", lambda: dspark((7, 13), 3, 2, hq=4, hkv=1, d=4, seed=4)),
+    ("mixed", lambda: SMALL_CASES["mixed_kinds"](hq=4, hkv=2, d=4, seed=5)),
 ]
 
 
@@ -528,3 +545,46 @@ def test_zigzag_plan_matches_hand_computed_fixture(fname):
         for key in PLAN_KEYS:
             assert np.array_equal(got[key], want[key]), (fname, r, key, got[key], want[key])
         assert zigzag.ring_bytes_received(cu, bcu, anchors, C, r, hkv, d, eb) == want["ring_bytes"][0]
+
+
+# ---------------------------------------------------------------------------
+# Mixed kinds: a packed batch equals its sequences run one by one, each with
+# its single kind (packed sequences never see each other)
+# ---------------------------------------------------------------------------
+
+def test_mixed_pack_equals_sequences_alone():
+    pack = SMALL_CASES["mixed_kinds"](hq=4, hkv=2, d=6, seed=11)
+    O, lse = oracle.forward(pack, block_pos=3)
+    dO = np.random.default_rng(5).standard_normal(O.shape)
+    dQ, dK, dV = oracle.backward(pack, dO, fwd=(O, lse), block_pos=3)
+    b0 = 0
+    for s, L in enumerate(MIXED["seqlens"]):
+        nA = len(MIXED["anchors"][s])
+        lens = MIXED["lens"][b0:b0 + nA]
+        kinds = set(MIXED["kinds"][b0:b0 + nA])
+        assert len(kinds) == 1
+        m = slice(int(pack.cu[s]), int(pack.cu[s + 1]))
+        br = slice(int(pack.bcu[b0]), int(pack.bcu[b0 + nA]))
+        alone = Problem([0, L], np.concatenate([[0], np.cumsum(lens)]), MIXED["anchors"][s],
+                        kinds.pop(), pack.hq, pack.hkv, pack.d, pack.q[m], pack.k[m], pack.v[m],
+                        pack.qb[br], pack.kb[br], pack.vb[br])
+        rows = np.concatenate([np.arange(m.start, m.stop), pack.N + np.arange(br.start, br.stop)])
+        o1, l1 = oracle.forward(alone, block_pos=3)
+        g1 = oracle.backward(alone, dO[rows], fwd=(o1, l1), block_pos=3)
+        assert np.allclose(O[rows], o1, atol=1e-13) and np.allclose(lse[rows], l1, atol=1e-13)
+        for full, one in zip((dQ, dK, dV), g1):
+            assert np.allclose(full[rows], one, atol=1e-12)
+        b0 += nA
+
+
+def test_mixed_pack_pair_count():
+    """Per-branch closed forms: main L(L+1)/2; a branch row sees its anchor's
+    position + 1 main keys; inside a branch B(B+1)/2 (causal) or B^2 (bidir)."""
+    pack = SMALL_CASES["mixed_kinds"](hq=2, hkv=1, d=2)
+    main = sum(L * (L + 1) // 2 for L in MIXED["seqlens"])
+    pos = [p for ps in MIXED["anchors"] for p in ps]
+    br_main = sum(B * (p + 1) for B, p in zip(MIXED["lens"], pos))
+    local = sum(B * (B + 1) // 2 if k == "causal" else B * B
+                for B, k in zip(MIXED["lens"], MIXED["kinds"]))
+    assert pack.count_visible() == main + br_main + local
+    assert brute.count_pairs(pack.cu, pack.bcu, pack.anchor, MIXED["kinds"]) == main + br_main + local
