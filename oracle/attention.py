@@ -211,16 +211,22 @@ def backward_rows(prob: Problem, rows, dO_rows, heads=None):
 
 
 def rows_seeing(prob: Problem, keys):
-    """Every query row that sees at least one of ``keys``."""
+    """Every query row that sees at least one of ``keys``.
+
+    Candidates: for each sequence holding a main key, its main rows and its
+    branch rows positioned at or after the earliest such key; the rows of
+    every branch holding a branch key.  The visibility rule then keeps the
+    candidates that see one of the keys."""
     kb, ks, kp, kbr, kt = prob.describe(keys)
     cand = []
-    for s, p in set(zip(ks[~kb].tolist(), kp[~kb].tolist())):
-        cand.append(prob.cu[s] + np.arange(p, prob.cu[s + 1] - prob.cu[s], dtype=np.int64))
-        sel = np.nonzero((prob.anchor_seq == s) & (prob.anchor_pos >= p))[0]
-        for a in sel:
-            cand.append(prob.N + np.arange(prob.bcu[a], prob.bcu[a + 1], dtype=np.int64))
-    for a in set(kbr[kb].tolist()):
-        cand.append(prob.N + np.arange(prob.bcu[a], prob.bcu[a + 1], dtype=np.int64))
+    for s in set(ks[~kb].tolist()):
+        p0 = int(kp[~kb][ks[~kb] == s].min())
+        cand.append(prob.cu[s] + np.arange(p0, prob.cu[s + 1] - prob.cu[s], dtype=np.int64))
+        if prob.Nb:
+            sel = (prob.anchor_seq == s) & (prob.anchor_pos >= p0)          # per branch
+            cand.append(prob.N + np.nonzero(sel[prob.branch_of_tok])[0])
+    if kb.any() and prob.Nb:
+        cand.append(prob.N + np.nonzero(np.isin(prob.branch_of_tok, kbr[kb]))[0])
     if not cand:
         return np.zeros(0, np.int64)
     rows = np.unique(np.concatenate(cand))
@@ -228,12 +234,17 @@ def rows_seeing(prob: Problem, keys):
     return rows[vis]
 
 
-def key_grads(prob: Problem, keys, dO_source, heads=None, row_chunk=64):
+def key_grads(prob: Problem, keys, dO_source, heads=None, row_chunk=64, rows=None):
     """dK, dV [len(keys), Hkv, d] for selected keys, summed over every row that
     sees them.  ``dO_source[ids]`` returns dO rows [.., Hq, d] for row ids.
-    ``heads`` optionally restricts the sum to those q-heads (all by default)."""
+    ``heads`` optionally restricts the sum to those q-heads (all by default);
+    ``rows`` optionally restricts it to those query rows -- the share of the
+    key gradients that one rank's rows produce in a ring, whose sum over the
+    ranks is the whole.  Each row's lse and Delta are still over its full
+    visible key set."""
     keys = np.asarray(keys, dtype=np.int64)
-    rows = rows_seeing(prob, keys)
+    rows_all = rows_seeing(prob, keys)
+    rows = rows_all if rows is None else np.intersect1d(rows_all, np.asarray(rows, np.int64))
     dK = np.zeros((keys.shape[0], prob.hkv, prob.d))
     dV = np.zeros((keys.shape[0], prob.hkv, prob.d))
     for i in range(0, rows.shape[0], row_chunk):

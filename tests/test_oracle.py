@@ -487,6 +487,22 @@ def test_sampled_rows_and_keys_agree_with_full():
     dO1[:, 2:] = 0
     _, dK1, dV1 = oracle.backward(prob, dO1, fwd=(O, lse))
     assert np.max(np.abs(dk1 - dK1[keys])) < 1e-12 and np.max(np.abs(dv1 - dV1[keys])) < 1e-12
+    # restricted to one zigzag rank's rows: equal to the definition with the
+    # other rows' dO set to zero (their dS and P dO vanish), and the ranks'
+    # shares sum to the whole
+    C = 3
+    tot_k, tot_v = np.zeros_like(dk), np.zeros_like(dv)
+    for r in range(C):
+        pl = zigzag.plan(prob.cu, prob.bcu, prob.anchor, C, r)
+        mine = np.concatenate([pl["main_index"], prob.N + pl["branch_index"]])
+        dkr, dvr = oracle.key_grads(prob, keys, dO, row_chunk=7, rows=mine)
+        dOr = np.zeros_like(dO)
+        dOr[mine] = dO[mine]
+        _, dKr, dVr = oracle.backward(prob, dOr, fwd=(O, lse))
+        assert np.max(np.abs(dkr - dKr[keys])) < 1e-12 and np.max(np.abs(dvr - dVr[keys])) < 1e-12
+        tot_k += dkr
+        tot_v += dvr
+    assert np.max(np.abs(tot_k - dK[keys])) < 1e-12 and np.max(np.abs(tot_v - dV[keys])) < 1e-12
 
 
 # ---------------------------------------------------------------------------
