@@ -106,6 +106,7 @@ def pairs_rows_keys(row_seq, row_pos, key_seq, key_pos):
 def build_step(torch, api, ring, w, st, t, dev, timer):
     """Return (step_fn, work) for the workload; work holds algorithmic FLOPs
     per launch class and totals."""
+    from branch_aware_causal_amd import flops as flops_mod
     hq, hkv, d = w.hq, w.hkv, w.d
     C, r = w.cp, w.rank
     plans = ring.plan_all(st.cu_seqlens, st.branch_cu, st.branch_anchor, C)
@@ -129,8 +130,8 @@ def build_step(torch, api, ring, w, st, t, dev, timer):
         pm = pairs_rows_keys(pl["main_seq"], pl["main_pos"], ps["main_seq"], ps["main_pos"])
         pb = pairs_rows_keys(pl["branch_seq"], pl["branch_pos"], ps["main_seq"], ps["main_pos"])
         per_shard.append((pm, pb))
-    local = (int(np.sum(np.diff(pl["local_branch_cu"]) ** 2)) if st.kind == "bidir"
-             else int(np.sum(pl["branch_t"].astype(np.int64) + 1)))
+    local = flops_mod.pair_counts_rows([], [], pl["branch_t"], pl["local_branch_cu"], st.kind,
+                                       st.branch_kinds[pl["branch_ids"]])[2]
     main_pairs = sum(a + b for a, b in per_shard)
     total_pairs = main_pairs + local
     kb_branch = 2 * 2 * nb * hkv * d * 2   # branch fwd bytes are reported, not priced
@@ -156,6 +157,8 @@ def build_step(torch, api, ring, w, st, t, dev, timer):
         seq_b = i32(p["branch_seq"]).to(dev, non_blocking=True)
         pos_b = i32(p["branch_pos"]).to(dev, non_blocking=True)
         lbcu = i32(p["local_branch_cu"]).to(dev, non_blocking=True)
+        kinds = (i32(st.branch_kinds[p["branch_ids"]]).to(dev, non_blocking=True)
+                 if st.kind == "mixed" else None)
         kidx = []
         for sh in ri.shards:
             if C == 1:
@@ -177,7 +180,7 @@ def build_step(torch, api, ring, w, st, t, dev, timer):
         # (a5, a6) rank-local branch part, final merge and bf16 rounding
         timer("branch_fwd", local * hq * 4 * d, api.attn_branch_fwd, ri.q_br, ri.kb, ri.vb, lbcu,
               ri.max_branch_len, ri.kind, bufs["o_br_acc"], bufs["lse_br"], api.MERGE,
-              o_out=bufs["o_br"], nbytes=bytes_branch_fwd)
+              o_out=bufs["o_br"], nbytes=bytes_branch_fwd, branch_kinds=kinds)
         # (a7) Delta
         timer("delta", 0, api.attn_bwd_delta, bufs["o_main_acc"], ri.do_main, bufs["delta_main"],
               nbytes=bytes_delta(nm))
@@ -204,7 +207,8 @@ def build_step(torch, api, ring, w, st, t, dev, timer):
         # (a9) branch backward
         timer("branch_bwd", local * hq * 10 * d, api.attn_branch_bwd, ri.q_br, ri.kb, ri.vb, lbcu,
               ri.max_branch_len, ri.kind, ri.do_br, bufs["lse_br"], bufs["delta_br"],
-              bufs["dq_br"], bufs["dkb"], bufs["dvb"], nbytes=bytes_branch_bwd)
+              bufs["dq_br"], bufs["dkb"], bufs["dvb"], nbytes=bytes_branch_bwd,
+              branch_kinds=kinds)
 
     return step, work, ri, pl, bufs
 
@@ -263,7 +267,7 @@ def cpu_baseline(w, st, t, n_anchor, log_fn):
 
     k = t["k"].float().cpu().numpy()
     v = t["v"].float().cpu().numpy()
-    prob = Problem(st.cu_seqlens, st.branch_cu, st.branch_anchor, st.kind, w.hq, w.hkv, w.d,
+    prob = Problem(st.cu_seqlens, st.branch_cu, st.branch_anchor, st.kind_names, w.hq, w.hkv, w.d,
                    Sparse(t["q"], main_rows), k, v, Sparse(t["qb"], br_tok), Sparse(t["kb"], br_tok),
                    Sparse(t["vb"], br_tok))
     dO = np.concatenate([t["do"].index_select(0, torch.as_tensor(main_rows, device=t["do"].device))

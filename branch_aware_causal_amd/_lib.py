@@ -35,7 +35,7 @@ SIGNATURES = {
                           C.POINTER(PlanOut)],
     "attn_main_fwd": [vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                       vp, vp, i32, vp, vp],
-    "attn_branch_fwd": [vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+    "attn_branch_fwd": [vp, vp, vp, i32, vp, i32, i32, i32, vp, i32, i32, i32, i32, f32,
                         vp, vp, i32, vp, vp],
     "lse_merge": [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp],
     "attn_bwd_delta": [vp, i32, vp, i32, i32, i32, i32, vp, vp],
@@ -45,7 +45,7 @@ SIGNATURES = {
                          vp, vp, vp, vp, vp],
     "attn_main_bwd_dkdv": [vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                            vp, vp, vp, vp, vp, vp],
-    "attn_branch_bwd": [vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+    "attn_branch_bwd": [vp, vp, vp, i32, vp, i32, i32, i32, vp, i32, i32, i32, i32, f32,
                         vp, vp, vp, vp, vp, vp, vp],
     "attn_check_index": [vp, vp, i32, i32, vp, vp],
     "bac_version": [],

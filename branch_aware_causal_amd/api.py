@@ -18,7 +18,8 @@ WRITE, MERGE = 0, 1
 CAUSAL, BIDIR = 0, 1
 
 _MODES = {"write": WRITE, "merge": MERGE, WRITE: WRITE, MERGE: MERGE}
-_KINDS = {"causal": CAUSAL, "bidir": BIDIR, CAUSAL: CAUSAL, BIDIR: BIDIR}
+# "mixed": per-branch kinds come in branch_kinds; the default kind is unused
+_KINDS = {"causal": CAUSAL, "bidir": BIDIR, "mixed": CAUSAL, CAUSAL: CAUSAL, BIDIR: BIDIR}
 
 
 class BacError(RuntimeError):
@@ -125,8 +126,15 @@ def attn_main_fwd(q, q_seq, q_pos, k, v, k_seq, k_pos, o_acc, lse, mode="write",
     _check(st)
 
 
+def _branch_kinds(branch_kinds, A):
+    """Per-branch kinds (device int32 [A], or None for one kind for all)."""
+    if branch_kinds is not None:
+        _need(branch_kinds, "branch_kinds", _torch().int32, (A,))
+    return _ptr(branch_kinds)
+
+
 def attn_branch_fwd(qb, kb, vb, branch_cu, max_branch_len, kind, o_acc, lse, mode="write",
-                    o_out=None, scale=None, stream=None):
+                    o_out=None, scale=None, stream=None, branch_kinds=None):
     nb, hq, d = qb.shape
     hkv = kb.shape[1]
     torch = _torch()
@@ -136,12 +144,13 @@ def attn_branch_fwd(qb, kb, vb, branch_cu, max_branch_len, kind, o_acc, lse, mod
     _need(vb, "vb", qb.dtype, (nb, hkv, d))
     _need(branch_cu, "branch_cu", torch.int32)
     A = branch_cu.shape[0] - 1
+    kinds = _branch_kinds(branch_kinds, A)
     _need(o_acc, "o_acc", torch.float32, (nb, hq, d))
     _need(lse, "lse", torch.float32, (hq, nb))
     if o_out is not None:
         _need(o_out, "o_out", qb.dtype, (nb, hq, d))
     st = _lib.load().attn_branch_fwd(_ptr(qb), _ptr(kb), _ptr(vb), nb, _ptr(branch_cu), A,
-                                     int(max_branch_len), _KINDS[kind], hq, hkv, d, dt,
+                                     int(max_branch_len), _KINDS[kind], kinds, hq, hkv, d, dt,
                                      _scale(scale, d), _ptr(o_acc), _ptr(lse), _MODES[mode],
                                      _ptr(o_out), _stream(stream))
     _check(st)
@@ -229,7 +238,7 @@ def attn_main_bwd_dkdv(q, q_seq, q_pos, k, v, k_seq, k_pos, dout, lse, delta, dk
 
 
 def attn_branch_bwd(qb, kb, vb, branch_cu, max_branch_len, kind, doutb, lseb, deltab, dqb, dkb,
-                    dvb, scale=None, stream=None):
+                    dvb, scale=None, stream=None, branch_kinds=None):
     nb, hq, d = qb.shape
     hkv = kb.shape[1]
     torch = _torch()
@@ -245,8 +254,9 @@ def attn_branch_bwd(qb, kb, vb, branch_cu, max_branch_len, kind, doutb, lseb, de
     _need(dqb, "dqb", torch.float32, (nb, hq, d))
     _need(dkb, "dkb", torch.float32, (nb, hkv, d))
     _need(dvb, "dvb", torch.float32, (nb, hkv, d))
+    kinds = _branch_kinds(branch_kinds, A)
     st = _lib.load().attn_branch_bwd(_ptr(qb), _ptr(kb), _ptr(vb), nb, _ptr(branch_cu), A,
-                                     int(max_branch_len), _KINDS[kind], hq, hkv, d, dt,
+                                     int(max_branch_len), _KINDS[kind], kinds, hq, hkv, d, dt,
                                      _scale(scale, d), _ptr(doutb), _ptr(lseb), _ptr(deltab),
                                      _ptr(dqb), _ptr(dkb), _ptr(dvb), _stream(stream))
     _check(st)

@@ -38,14 +38,8 @@ static bac_status hip_status(hipError_t e, const char* where) {
   return fail(BAC_EHIP, "%s: HIP error %d (%s)", where, static_cast<int>(e), hipGetErrorString(e));
 }
 
-// Optional override of the bf16 main-attention implementation: the
-// BAC_MAIN_IMPL environment variable set to "valu" selects the vector-ALU
-// kernels (a slow second GPU implementation used for cross-checks).
-static bool main_uses_valu(int dt) {
-  if (dt == kF32) return true;
-  const char* e = std::getenv("BAC_MAIN_IMPL");
-  return e && std::strcmp(e, "valu") == 0;
-}
+// fp32 main attention runs on the vector-ALU kernels, bf16 on MFMA.
+static bool main_uses_valu(int dt) { return dt == kF32; }
 
 static bac_status check_heads(const char* fn, int32_t hq, int32_t hkv, int32_t d, int32_t dt) {
   if (hq < 1 || hkv < 1) return fail(BAC_EINVAL, "%s: hq=%d hkv=%d must be >= 1", fn, hq, hkv);
@@ -72,6 +66,14 @@ static bac_status check_aligned(const char* fn, std::initializer_list<const void
   return BAC_OK;
 }
 
+// The softmax scale must be finite and positive: the MFMA forward masks a
+// score to -inf before scaling and takes the row maximum of unscaled scores.
+static bac_status check_scale(const char* fn, float scale) {
+  if (!std::isfinite(scale)) return fail(BAC_EINVAL, "%s: scale is not finite", fn);
+  if (!(scale > 0.f)) return fail(BAC_EUNSUPPORTED, "%s: scale %g is not positive", fn, scale);
+  return BAC_OK;
+}
+
 #define BAC_TRY(expr)              \
   do {                             \
     bac_status _st = (expr);       \
@@ -87,9 +89,12 @@ static bac_status check_main(const char* fn, const void* q, const int32_t* q_seq
   BAC_TRY(check_count(fn, "nk", nk, hq));
   if (nq > 0 && (!q || !q_seq || !q_pos)) return fail(BAC_EINVAL, "%s: null query array", fn);
   if (nk > 0 && (!k || !v || !k_seq || !k_pos)) return fail(BAC_EINVAL, "%s: null key array", fn);
-  if (!std::isfinite(scale)) return fail(BAC_EINVAL, "%s: scale is not finite", fn);
+  BAC_TRY(check_scale(fn, scale));
   return BAC_OK;
 }
+
+// Longest branch the branch kernels accept (one wave walks a branch's tokens).
+constexpr int32_t kMaxBranchLen = 256;
 
 static bac_status check_branch(const char* fn, const void* qb, const void* kb, const void* vb,
                                int32_t nb, const int32_t* branch_cu, int32_t num_branches,
@@ -102,9 +107,10 @@ static bac_status check_branch(const char* fn, const void* qb, const void* kb, c
   if (nb > 0 && (!qb || !kb || !vb)) return fail(BAC_EINVAL, "%s: null branch tensor", fn);
   if (kind != BAC_BRANCH_CAUSAL && kind != BAC_BRANCH_BIDIR)
     return fail(BAC_EINVAL, "%s: unknown branch kind %d", fn, kind);
-  if (max_len < 1 || max_len > 32)
-    return fail(BAC_EUNSUPPORTED, "%s: max_branch_len=%d outside [1, 32]", fn, max_len);
-  if (!std::isfinite(scale)) return fail(BAC_EINVAL, "%s: scale is not finite", fn);
+  if (max_len < 1 || max_len > kMaxBranchLen)
+    return fail(BAC_EUNSUPPORTED, "%s: max_branch_len=%d outside [1, %d]", fn, max_len,
+                kMaxBranchLen);
+  BAC_TRY(check_scale(fn, scale));
   return BAC_OK;
 }
 
@@ -141,9 +147,9 @@ bac_status attn_main_fwd(const void* q, const int32_t* q_seq, const int32_t* q_p
 
 bac_status attn_branch_fwd(const void* qb, const void* kb, const void* vb, int32_t nb,
                            const int32_t* branch_cu, int32_t num_branches, int32_t max_branch_len,
-                           bac_branch_kind kind, int32_t hq, int32_t hkv, int32_t d, bac_dtype dt,
-                           float scale, float* o_acc, float* lse, bac_acc_mode mode, void* o_out,
-                           void* stream) {
+                           bac_branch_kind kind, const int32_t* branch_kinds, int32_t hq,
+                           int32_t hkv, int32_t d, bac_dtype dt, float scale, float* o_acc,
+                           float* lse, bac_acc_mode mode, void* o_out, void* stream) {
   clear_error();
   const char* fn = "attn_branch_fwd";
   BAC_TRY(check_branch(fn, qb, kb, vb, nb, branch_cu, num_branches, max_branch_len, kind, hq, hkv,
@@ -156,6 +162,7 @@ bac_status attn_branch_fwd(const void* qb, const void* kb, const void* vb, int32
   a.qb = qb; a.kb = kb; a.vb = vb; a.nb = nb;
   a.branch_cu = branch_cu; a.num_branches = num_branches; a.max_len = max_branch_len;
   a.bidir = kind == BAC_BRANCH_BIDIR;
+  a.kinds = branch_kinds;
   a.hq = hq; a.hkv = hkv; a.d = d; a.dt = dt; a.scale = scale;
   a.o_acc = o_acc; a.lse_acc = lse; a.mode = mode; a.o_out = o_out;
   a.stream = static_cast<hipStream_t>(stream);
@@ -254,9 +261,10 @@ bac_status attn_main_bwd_dkdv(const void* q, const int32_t* q_seq, const int32_t
 
 bac_status attn_branch_bwd(const void* qb, const void* kb, const void* vb, int32_t nb,
                            const int32_t* branch_cu, int32_t num_branches, int32_t max_branch_len,
-                           bac_branch_kind kind, int32_t hq, int32_t hkv, int32_t d, bac_dtype dt,
-                           float scale, const void* doutb, const float* lseb, const float* deltab,
-                           float* dqb_acc, float* dkb_acc, float* dvb_acc, void* stream) {
+                           bac_branch_kind kind, const int32_t* branch_kinds, int32_t hq,
+                           int32_t hkv, int32_t d, bac_dtype dt, float scale, const void* doutb,
+                           const float* lseb, const float* deltab, float* dqb_acc,
+                           float* dkb_acc, float* dvb_acc, void* stream) {
   clear_error();
   const char* fn = "attn_branch_bwd";
   BAC_TRY(check_branch(fn, qb, kb, vb, nb, branch_cu, num_branches, max_branch_len, kind, hq, hkv,
@@ -269,6 +277,7 @@ bac_status attn_branch_bwd(const void* qb, const void* kb, const void* vb, int32
   a.qb = qb; a.kb = kb; a.vb = vb; a.nb = nb;
   a.branch_cu = branch_cu; a.num_branches = num_branches; a.max_len = max_branch_len;
   a.bidir = kind == BAC_BRANCH_BIDIR;
+  a.kinds = branch_kinds;
   a.hq = hq; a.hkv = hkv; a.d = d; a.dt = dt; a.scale = scale;
   a.dout = doutb; a.lse = lseb; a.delta = deltab; a.dq = dqb_acc; a.dk = dkb_acc; a.dv = dvb_acc;
   a.stream = static_cast<hipStream_t>(stream);

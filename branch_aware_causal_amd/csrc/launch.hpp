@@ -46,7 +46,8 @@ struct BranchArgs {
   const int32_t* branch_cu;
   int num_branches;
   int max_len;
-  int bidir;
+  int bidir;                   // kind of every branch when kinds is null
+  const int32_t* kinds;        // per-branch kind (device) or null
   int hq, hkv, d;
   int dt;
   float scale;

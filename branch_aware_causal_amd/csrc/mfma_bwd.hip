@@ -489,8 +489,11 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
     } else {
       const int r = min(lane, TR - 1);
       const int tok = min(r / G, tmax);
-      const uint32_t off = 4u * static_cast<uint32_t>(kg < 2 ? (g * G + r % G) * nq + tok : tok);
-      dma_b32(meta_src + static_cast<size_t>(t0) * 4, off, lds_addr(&Mr[st][kg * MS]));
+      // lse / Delta are [hq, nq]: a 64-bit element index, since (head * nq)
+      // exceeds 32 bits of bytes once hq * nq reaches 2^30
+      const size_t idx = static_cast<size_t>(t0 + tok) +
+                         (kg < 2 ? static_cast<size_t>(g * G + r % G) * nq : 0);
+      dma_b32_at(meta_src + 4 * idx, lds_addr(&Mr[st][kg * MS]));
     }
   };
   auto issue = [&](int st, int i) {

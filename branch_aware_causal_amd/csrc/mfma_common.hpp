@@ -227,5 +227,11 @@ __device__ __forceinline__ void dma_b32(const void* base, uint32_t voff, uint32_
                :: "v"(voff), "s"(uniform_ptr(base)), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
+// Same with a full 64-bit per-lane address (no scalar base).
+__device__ __forceinline__ void dma_b32_at(const void* addr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(addr), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
 
 }  // namespace bac

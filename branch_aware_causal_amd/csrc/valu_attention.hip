@@ -146,7 +146,9 @@ __global__ __launch_bounds__(256) void branch_fwd_kernel(const T* __restrict__ q
                                                          const T* __restrict__ kb,
                                                          const T* __restrict__ vb, int nb,
                                                          const int32_t* __restrict__ bcu, int A,
-                                                         int max_len, int bidir, int hq, int hkv,
+                                                         int max_len, int bidir_all,
+                                                         const int32_t* __restrict__ kinds,
+                                                         int hq, int hkv,
                                                          float scale_log2, float* o_acc,
                                                          float* lse_acc, int mode, T* o_out) {
   constexpr int LPR = D / 8;       // lanes per row
@@ -154,6 +156,7 @@ __global__ __launch_bounds__(256) void branch_fwd_kernel(const T* __restrict__ q
   const int lane = threadIdx.x & 63;
   const int a = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (a >= A) return;
+  const bool bidir = kinds ? kinds[a] == 1 : bidir_all != 0;   // 1 = BAC_BRANCH_BIDIR
   const int g = blockIdx.y;
   const int G = hq / hkv;
   const int r = lane / LPR, col = 8 * (lane % LPR);
@@ -228,7 +231,8 @@ __global__ __launch_bounds__(256) void branch_fwd_kernel(const T* __restrict__ q
 template <typename T, int D>
 __global__ __launch_bounds__(256) void branch_bwd_kernel(
     const T* __restrict__ qb, const T* __restrict__ kb, const T* __restrict__ vb, int nb,
-    const int32_t* __restrict__ bcu, int A, int max_len, int bidir, int hq, int hkv, float scale,
+    const int32_t* __restrict__ bcu, int A, int max_len, int bidir_all,
+    const int32_t* __restrict__ kinds, int hq, int hkv, float scale,
     const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     float* dq, float* dk, float* dv) {
   constexpr int LPR = D / 8;       // lanes per row
@@ -236,6 +240,7 @@ __global__ __launch_bounds__(256) void branch_bwd_kernel(
   const int lane = threadIdx.x & 63;
   const int a = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (a >= A) return;
+  const bool bidir = kinds ? kinds[a] == 1 : bidir_all != 0;   // 1 = BAC_BRANCH_BIDIR
   const int g = blockIdx.y;
   const int G = hq / hkv;
   const int r = lane / LPR, col = 8 * (lane % LPR);
@@ -347,7 +352,8 @@ __global__ __launch_bounds__(256) void branch_bwd_kernel(
 template <typename T, int D, int MAXL>
 __global__ __launch_bounds__(256) void branch_bwd_short_kernel(
     const T* __restrict__ qb, const T* __restrict__ kb, const T* __restrict__ vb, int nb,
-    const int32_t* __restrict__ bcu, int A, int max_len, int bidir, int hq, int hkv, float scale,
+    const int32_t* __restrict__ bcu, int A, int max_len, int bidir_all,
+    const int32_t* __restrict__ kinds, int hq, int hkv, float scale,
     const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     float* dq, float* dk, float* dv) {
   constexpr int LPR = D / 8;       // lanes per row
@@ -355,6 +361,7 @@ __global__ __launch_bounds__(256) void branch_bwd_short_kernel(
   const int lane = threadIdx.x & 63;
   const int a = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (a >= A) return;
+  const bool bidir = kinds ? kinds[a] == 1 : bidir_all != 0;   // 1 = BAC_BRANCH_BIDIR
   const int g = blockIdx.y;
   const int G = hq / hkv;
   const int r = lane / LPR, col = 8 * (lane % LPR);
@@ -451,7 +458,7 @@ static void branch_fwd_d(const BranchArgs& a) {
   hipLaunchKernelGGL((branch_fwd_kernel<T, D>), grid, dim3(256), 0, a.stream,
                      static_cast<const T*>(a.qb), static_cast<const T*>(a.kb),
                      static_cast<const T*>(a.vb), a.nb, a.branch_cu, a.num_branches, a.max_len,
-                     a.bidir, a.hq, a.hkv, a.scale * kLog2e, a.o_acc, a.lse_acc, a.mode,
+                     a.bidir, a.kinds, a.hq, a.hkv, a.scale * kLog2e, a.o_acc, a.lse_acc, a.mode,
                      static_cast<T*>(a.o_out));
 }
 
@@ -474,14 +481,15 @@ static void branch_bwd_d(const BranchArgs& a) {
     hipLaunchKernelGGL((branch_bwd_short_kernel<T, D, 4>), grid, dim3(256), 0, a.stream,
                        static_cast<const T*>(a.qb), static_cast<const T*>(a.kb),
                        static_cast<const T*>(a.vb), a.nb, a.branch_cu, a.num_branches, a.max_len,
-                       a.bidir, a.hq, a.hkv, a.scale, static_cast<const T*>(a.dout), a.lse,
+                       a.bidir, a.kinds, a.hq, a.hkv, a.scale, static_cast<const T*>(a.dout), a.lse,
                        a.delta, a.dq, a.dk, a.dv);
     return;
   }
   hipLaunchKernelGGL((branch_bwd_kernel<T, D>), grid, dim3(256), 0, a.stream,
                      static_cast<const T*>(a.qb), static_cast<const T*>(a.kb),
                      static_cast<const T*>(a.vb), a.nb, a.branch_cu, a.num_branches, a.max_len,
-                     a.bidir, a.hq, a.hkv, a.scale, static_cast<const T*>(a.dout), a.lse, a.delta,
+                     a.bidir, a.kinds, a.hq, a.hkv, a.scale, static_cast<const T*>(a.dout), a.lse,
+                     a.delta,
                      a.dq, a.dk, a.dv);
 }
 

@@ -44,7 +44,8 @@ class RankInputs:
     vb: object
     branch_cu: object         # device int32 [n_local_branches + 1]
     max_branch_len: int
-    kind: str
+    kind: str                 # "causal", "bidir", or "mixed" (per-branch kinds below)
+    branch_kinds: object = None   # device int32 [n_local_branches] when mixed
     shards: List[Shard] = field(default_factory=list)
     do_main: object = None
     do_br: object = None
@@ -80,7 +81,8 @@ def forward(ri: RankInputs, scale=None, stream=None, out=None):
                           out["o_br_acc"], out["lse_br"], mode, scale=scale, stream=stream)
     api.attn_branch_fwd(ri.q_br, ri.kb, ri.vb, ri.branch_cu, ri.max_branch_len, ri.kind,
                         out["o_br_acc"], out["lse_br"], api.MERGE if C > 0 else api.WRITE,
-                        o_out=out["o_br"], scale=scale, stream=stream)
+                        o_out=out["o_br"], scale=scale, stream=stream,
+                        branch_kinds=ri.branch_kinds)
     return out
 
 
@@ -113,7 +115,7 @@ def backward(ri: RankInputs, fwd, scale=None, stream=None, grads=None, delta_fro
                           grads["dk"][s], grads["dv"][s], scale=scale, stream=stream)
     api.attn_branch_bwd(ri.q_br, ri.kb, ri.vb, ri.branch_cu, ri.max_branch_len, ri.kind,
                         ri.do_br, fwd["lse_br"], grads["delta_br"], grads["dq_br"], grads["dkb"],
-                        grads["dvb"], scale=scale, stream=stream)
+                        grads["dvb"], scale=scale, stream=stream, branch_kinds=ri.branch_kinds)
     return grads
 
 
@@ -154,6 +156,8 @@ def rank_inputs(struct, tensors, cp_size: int, rank: int, plans=None, device=Non
         kb=rows(tensors["kb"], pl["branch_index"]), vb=rows(tensors["vb"], pl["branch_index"]),
         branch_cu=i32(pl["local_branch_cu"]), max_branch_len=int(struct.max_branch_len),
         kind=struct.kind, shards=shards,
+        branch_kinds=(i32(np.asarray(struct.branch_kinds)[pl["branch_ids"]])
+                      if struct.kind == "mixed" else None),
         do_main=rows(tensors["do"], pl["main_index"]) if "do" in tensors else None,
         do_br=rows(tensors["dob"], pl["branch_index"]) if "dob" in tensors else None)
     return ri, pl

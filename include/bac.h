@@ -33,7 +33,10 @@
  * Types:     bac_dtype selects the element type of q, k, v, dout and o_out
  *            (fp32 or bf16).  Accumulators (o_acc, lse, dq/dk/dv) are fp32.
  * Limits:    d in {64, 128}; hq % hkv == 0 and hq / hkv divides 32;
- *            n < 2^31 / hq.
+ *            n * hq < 2^31 for every row count n (BAC_ESIZE otherwise).
+ * Scale:     the softmax scale of the attention calls is finite and
+ *            positive; 0 or a negative scale is BAC_EUNSUPPORTED, a
+ *            non-finite one BAC_EINVAL.
  * Checks:    host-side arguments are validated before anything is enqueued
  *            (BAC_EINVAL / BAC_EUNSUPPORTED, nothing launched).  The contents
  *            of device index arrays are preconditions; attn_check_index()
@@ -156,20 +159,27 @@ bac_status attn_main_fwd(const void* q, const int32_t* q_seq, const int32_t* q_p
  *
  * Branch a owns tokens [branch_cu[a], branch_cu[a+1]) of qb/kb/vb; token t of
  * the branch sees tokens 0..t of the same branch (CAUSAL) or all of them
- * (BIDIR).  No branch sees another.
+ * (BIDIR).  No branch sees another.  Each branch may have its own kind, so
+ * one call serves a pack that mixes EAGLE-3 chains, DFlash blocks and DSpark
+ * blocks ([G] 技术贡献: one design serves all three drafts).
  *
  * qb [nb, hq, d], kb/vb [nb, hkv, d]: device, dtype dt.
  * branch_cu [num_branches+1]: device int32, branch_cu[0] = 0,
  *   branch_cu[num_branches] = nb, non-decreasing.
- * max_branch_len: host bound on every branch's length, 1..32.  A longer branch
- *   is a precondition violation: its rows past the bound are left untouched.
+ * max_branch_len: host bound on every branch's length, 1..256.  A longer
+ *   branch is a precondition violation: its rows past the bound are left
+ *   untouched.
+ * kind: the kind of every branch when branch_kinds is NULL.
+ * branch_kinds: NULL, or device int32 [num_branches]: branch a is
+ *   bidirectional when branch_kinds[a] == BAC_BRANCH_BIDIR and causal for any
+ *   other value (kind is then ignored).
  * o_acc/lse/mode/o_out: as attn_main_fwd, rows = branch tokens.
  * ---------------------------------------------------------------------- */
 bac_status attn_branch_fwd(const void* qb, const void* kb, const void* vb, int32_t nb,
                            const int32_t* branch_cu, int32_t num_branches, int32_t max_branch_len,
-                           bac_branch_kind kind, int32_t hq, int32_t hkv, int32_t d, bac_dtype dt,
-                           float scale, float* o_acc, float* lse, bac_acc_mode mode, void* o_out,
-                           void* stream);
+                           bac_branch_kind kind, const int32_t* branch_kinds, int32_t hq,
+                           int32_t hkv, int32_t d, bac_dtype dt, float scale, float* o_acc,
+                           float* lse, bac_acc_mode mode, void* o_out, void* stream);
 
 /* ------------------------------------------------------------------------
  * lse_merge -- the online-softmax merge of [G] 技术贡献:
@@ -229,14 +239,16 @@ bac_status attn_main_bwd_dkdv(const void* q, const int32_t* q_seq, const int32_t
 /* ------------------------------------------------------------------------
  * attn_branch_bwd -- gradients of attn_branch_fwd's rows over their own
  * branch keys, from the merged lse/delta of those rows.  Arguments as
- * attn_branch_fwd plus doutb [nb, hq, d], lseb / deltab [hq, nb] and fp32
- * accumulators dqb_acc [nb, hq, d], dkb_acc / dvb_acc [nb, hkv, d] (added to).
+ * attn_branch_fwd (kind / branch_kinds included) plus doutb [nb, hq, d],
+ * lseb / deltab [hq, nb] and fp32 accumulators dqb_acc [nb, hq, d],
+ * dkb_acc / dvb_acc [nb, hkv, d] (added to).
  * ---------------------------------------------------------------------- */
 bac_status attn_branch_bwd(const void* qb, const void* kb, const void* vb, int32_t nb,
                            const int32_t* branch_cu, int32_t num_branches, int32_t max_branch_len,
-                           bac_branch_kind kind, int32_t hq, int32_t hkv, int32_t d, bac_dtype dt,
-                           float scale, const void* doutb, const float* lseb, const float* deltab,
-                           float* dqb_acc, float* dkb_acc, float* dvb_acc, void* stream);
+                           bac_branch_kind kind, const int32_t* branch_kinds, int32_t hq,
+                           int32_t hkv, int32_t d, bac_dtype dt, float scale, const void* doutb,
+                           const float* lseb, const float* deltab, float* dqb_acc,
+                           float* dkb_acc, float* dvb_acc, void* stream);
 
 /* ------------------------------------------------------------------------
  * attn_check_index -- device-side validation of the index preconditions.

@@ -73,7 +73,7 @@ def problem(st, t, lazy=False):
     """Oracle problem on the exact (bf16-rounded) input values."""
     hq, hkv, d = t["q"].shape[1], t["k"].shape[1], t["q"].shape[2]
     src = (lambda x: numpy_rows(x)) if lazy else host64
-    return Problem(st.cu_seqlens, st.branch_cu, st.branch_anchor, st.kind, hq, hkv, d,
+    return Problem(st.cu_seqlens, st.branch_cu, st.branch_anchor, st.kind_names, hq, hkv, d,
                    src(t["q"]), src(t["k"]), src(t["v"]), src(t["qb"]), src(t["kb"]), src(t["vb"]))
 
 
@@ -124,3 +124,86 @@ def check_rne(gpu):
             assert torch.equal(gpu[acc].to(torch.bfloat16), gpu[out]), out
         else:
             assert torch.equal(gpu[acc], gpu[out]), out
+
+
+def workers():
+    """Host threads for the oracle: the machine's CPU share is 16 cores."""
+    import os
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _parallel(fn, parts):
+    """fn over parts on a thread pool, one BLAS thread per worker (NumPy
+    releases the GIL inside BLAS and large elementwise loops)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=workers()) as ex:
+        return list(ex.map(fn, parts))
+
+
+def par_backward_rows(prob, rows, dO_rows, heads=None, chunk=32):
+    """oracle.backward_rows over row chunks in parallel: (dq, O, lse) in the
+    order of ``rows``.  Rows are grouped by (sequence, position) -- a branch
+    row sits at its anchor -- so a chunk's rows share most of their keys."""
+    rows = np.asarray(rows, np.int64)
+    _, seq, pos, _, _ = prob.describe(rows)
+    order = np.lexsort((pos, seq))
+    idx = [order[i:i + chunk] for i in range(0, rows.size, chunk)]
+    res = _parallel(lambda ii: oracle.backward_rows(prob, rows[ii], dO_rows[ii], heads=heads), idx)
+    out = []
+    for j in range(3):
+        cat = np.concatenate([r[j] for r in res])
+        back = np.empty_like(cat)
+        back[order] = cat
+        out.append(back)
+    return tuple(out)
+
+
+def full_group_reference(prob, dO_rows_fn, group=0, block_pos=128):
+    """Definition mode over the whole problem for one kv-head group: O, lse
+    and dQ of every row on the group's q-heads, dK and dV of every key of
+    kv-head `group`.  Blocks of positions run in parallel; dO_rows_fn(rows)
+    returns dO [len(rows), Hq, d] (fp64)."""
+    from oracle.attention import _blocks, delta, grads, partial
+    G = prob.hq // prob.hkv
+    heads = list(range(group * G, (group + 1) * G))
+    n = prob.N + prob.Nb
+    blocks = list(_blocks(prob, block_pos))
+
+    import threading
+    lock = threading.Lock()
+    O = np.zeros((n, G, prob.d))
+    lse = np.full((n, G), -np.inf)
+    dQ = np.zeros((n, G, prob.d))
+    dK = np.zeros((n, prob.d))
+    dV = np.zeros((n, prob.d))
+
+    def run(rk):
+        rows, keys = rk
+        o, l = partial(prob, rows, keys, heads)
+        dO = np.zeros((rows.size, prob.hq, prob.d))
+        dO[:, heads] = dO_rows_fn(rows)[:, heads]
+        dq, dk, dv = grads(prob, rows, keys, l, dO, delta(o, dO), heads)
+        with lock:      # a block's rows are its own; its keys recur in later blocks
+            O[rows], lse[rows] = o[:, heads], l[:, heads]
+            dQ[rows] += dq[:, heads]
+            dK[keys] += dk[:, group]
+            dV[keys] += dv[:, group]
+
+    _parallel(run, blocks)
+    return O, lse, dQ, dK, dV
+
+
+def par_key_grads(prob, keys, dO_source, heads=None, rows=None, row_chunk=64):
+    """oracle.key_grads with its rows split over the workers, summed."""
+    from oracle.attention import rows_seeing
+    keys = np.asarray(keys, np.int64)
+    cand = rows_seeing(prob, keys)
+    if rows is not None:
+        cand = np.intersect1d(cand, np.asarray(rows, np.int64))
+    n = max(1, min(workers() * 4, cand.size // row_chunk + 1))
+    # interleave so every part gets early and late (short and long) rows
+    parts = [cand[i::n] for i in range(n)]
+    res = _parallel(lambda part: oracle.key_grads(prob, keys, dO_source, heads=heads,
+                                                  row_chunk=row_chunk, rows=part), parts)
+    return sum(r[0] for r in res), sum(r[1] for r in res)

@@ -68,7 +68,11 @@ def _call_main_fwd(lib, **over):
     (dict(nq=-1), -1, "negative"),
     (dict(o_acc=None), -1, "o_acc"),
     (dict(scale=float("inf")), -1, "scale"),
+    (dict(scale=0.0), -2, "not positive"),
+    (dict(scale=-0.1), -2, "not positive"),
     (dict(nq=2**29, hq=8), -3, "2^31"),
+    (dict(nq=2**28, hq=8), -3, "2^31"),      # n * hq = 2^31 exactly
+    (dict(nk=2**26, hq=32), -3, "2^31"),
 ])
 def test_main_fwd_rejects_bad_arguments(lib, over, code, needle):
     from branch_aware_causal_amd import _lib
@@ -82,8 +86,8 @@ def test_misaligned_tensors_are_rejected_before_launch(lib):
     assert _call_main_fwd(lib, q=24, k=32, v=48, o_acc=64) == -1
     assert "16-byte aligned" in _lib.last_error()
     vp = C.c_void_p
-    st = lib.attn_branch_fwd(vp(16), vp(40), vp(48), 8, vp(4), 2, 3, 0, 8, 2, 128, 1, 0.1, vp(64),
-                             vp(4), 0, vp(None), vp(None))
+    st = lib.attn_branch_fwd(vp(16), vp(40), vp(48), 8, vp(4), 2, 3, 0, vp(None), 8, 2, 128, 1,
+                             0.1, vp(64), vp(4), 0, vp(None), vp(None))
     assert st == -1 and "16-byte aligned" in _lib.last_error()
     st = lib.lse_merge(vp(16), vp(4), vp(36), vp(4), 4, 8, 128, 1, vp(None), vp(None))
     assert st == -1 and "16-byte aligned" in _lib.last_error()
@@ -101,12 +105,19 @@ def test_branch_and_merge_validation(lib):
     from branch_aware_causal_amd import _lib
     vp = C.c_void_p
     # max_branch_len beyond the supported bound
-    st = lib.attn_branch_fwd(vp(1), vp(1), vp(1), 8, vp(1), 2, 33, 0, 8, 2, 128, 1, 0.1, vp(1),
-                             vp(1), 0, vp(None), vp(None))
+    st = lib.attn_branch_fwd(vp(1), vp(1), vp(1), 8, vp(1), 2, 257, 0, vp(None), 8, 2, 128, 1,
+                             0.1, vp(1), vp(1), 0, vp(None), vp(None))
     assert st == -2 and "max_branch_len" in _lib.last_error()
-    st = lib.attn_branch_bwd(vp(1), vp(1), vp(1), 8, vp(1), 2, 4, 5, 8, 2, 128, 1, 0.1, vp(1),
-                             vp(1), vp(1), vp(1), vp(1), vp(1), vp(None))
+    st = lib.attn_branch_bwd(vp(1), vp(1), vp(1), 8, vp(1), 2, 4, 5, vp(None), 8, 2, 128, 1, 0.1,
+                             vp(1), vp(1), vp(1), vp(1), vp(1), vp(1), vp(None))
     assert st == -1 and "kind" in _lib.last_error()
+    for bad in (0.0, -1.0):
+        st = lib.attn_branch_fwd(vp(16), vp(16), vp(16), 8, vp(4), 2, 4, 0, vp(None), 8, 2, 128,
+                                 1, bad, vp(16), vp(4), 0, vp(None), vp(None))
+        assert st == -2 and "not positive" in _lib.last_error()
+        st = lib.attn_main_bwd(vp(16), vp(4), vp(4), 4, vp(16), vp(16), vp(4), vp(4), 4, 8, 2, 128,
+                               1, bad, vp(16), vp(4), vp(4), vp(16), vp(16), vp(16), vp(None))
+        assert st == -2 and "not positive" in _lib.last_error()
     st = lib.lse_merge(vp(1), vp(1), vp(1), vp(1), 4, 8, 128, 1, vp(None), vp(None))
     assert st == -1 and "alias" in _lib.last_error()
     st = lib.attn_main_bwd(vp(1), vp(1), vp(1), 4, vp(1), vp(1), vp(1), vp(1), 4, 8, 2, 128, 1,

@@ -13,7 +13,7 @@ from workloads.gen import make_structure_custom
 
 def _prob(st, hq=2, hkv=1, d=2):
     z = lambda n, h: np.zeros((n, h, d))
-    return Problem(st.cu_seqlens, st.branch_cu, st.branch_anchor, st.kind, hq, hkv, d,
+    return Problem(st.cu_seqlens, st.branch_cu, st.branch_anchor, st.kind_names, hq, hkv, d,
                    z(st.n_main, hq), z(st.n_main, hkv), z(st.n_main, hkv),
                    z(st.n_branch_tok, hq), z(st.n_branch_tok, hkv), z(st.n_branch_tok, hkv))
 
@@ -26,6 +26,16 @@ def _prob(st, hq=2, hkv=1, d=2):
 def test_pair_counts_match_visibility(st):
     assert sum(flops.pair_counts(st.cu_seqlens, st.branch_cu, st.branch_anchor, st.kind)) == \
         _prob(st).count_visible()
+
+
+def test_mixed_pack_pair_counts_match_visibility():
+    from workloads import specs
+    w = specs.small("mix", (40, 48, 24), branch="mixed",
+                    mix=(("eagle3", 3, 1), ("dflash", 16, 16), ("dspark", 8, 8)))
+    st = make_structure(w)
+    assert st.kind == "mixed" and set(st.branch_kinds.tolist()) == {0, 1}
+    got = flops.pair_counts(st.cu_seqlens, st.branch_cu, st.branch_anchor, st.kind, st.branch_kinds)
+    assert sum(got) == _prob(st).count_visible()
 
 
 @pytest.mark.parametrize("C", [2, 4])

@@ -2,7 +2,7 @@
 
 Small and medium problems, compared element by element with the full oracle
 (definition mode): several 64-key tiles, ragged tails, every branch kind,
-GQA ratios 1..8, head dims 64 and 128, fp32 and bf16, zigzag rings.
+every GQA ratio 1..32, head dims 64 and 128, fp32 and bf16, zigzag rings.
 Tolerances (max abs): bf16 2e-2 on O and gradients (fp32 accumulators),
 fp32 1e-5, lse 1e-3; masks and indices bit-exact.
 """
@@ -51,6 +51,36 @@ SMALL = {
     "eagle3_long_rows_bf16": specs.small("long", (2600, 300), hq=4, hkv=1, d=128, dtype="bf16",
                                          branch="eagle3", branch_len=2, value_scale=0.5,
                                          seed_base=1700),
+    # every GQA ratio the MFMA kernels are built for (hq / hkv = 2, 16, 32),
+    # each at both head dims, with ragged lengths
+    "eagle3_gqa2_d64_bf16": specs.small("q2a", (130, 67, 5), hq=4, hkv=2, d=64, dtype="bf16",
+                                        branch="eagle3", branch_len=3, seed_base=1800),
+    "dspark_gqa2_d128_bf16": specs.small("q2b", (200, 33), hq=4, hkv=2, d=128, dtype="bf16",
+                                         branch="dspark", branch_len=8, anchor_stride=8,
+                                         seed_base=1900),
+    "eagle3_gqa16_d128_bf16": specs.small("q16a", (90, 41), hq=32, hkv=2, d=128, dtype="bf16",
+                                          branch="eagle3", branch_len=2, seed_base=2000),
+    "dflash_gqa16_d64_bf16": specs.small("q16b", (96, 40), hq=32, hkv=2, d=64, dtype="bf16",
+                                         branch="dflash", branch_len=16, anchor_stride=16,
+                                         seed_base=2100),
+    "eagle3_gqa32_d64_bf16": specs.small("q32a", (77, 100, 3), hq=32, hkv=1, d=64, dtype="bf16",
+                                         branch="eagle3", branch_len=3, seed_base=2200),
+    "eagle3_gqa32_d128_bf16": specs.small("q32b", (150, 9), hq=32, hkv=1, d=128, dtype="bf16",
+                                          branch="eagle3", branch_len=2, seed_base=2300),
+    # one pack mixing the three families, each branch with its own kind
+    "mixed_kinds_bf16": specs.small("mix", (150, 96, 40), hq=8, hkv=2, d=128, dtype="bf16",
+                                    branch="mixed", seed_base=2400,
+                                    mix=(("eagle3", 3, 1), ("dflash", 16, 16), ("dspark", 8, 8))),
+    "mixed_kinds_f32": specs.small("mixf", (40, 33, 17), hq=4, hkv=2, d=64, dtype="f32",
+                                   branch="mixed", seed_base=2500,
+                                   mix=(("dspark", 4, 2), ("eagle3", 2, 1), ("dflash", 8, 8))),
+    # branches longer than 32 tokens (bidirectional blocks of 64, causal of 48)
+    "dflash_b64_bf16": specs.small("b64", (256, 130), hq=8, hkv=2, d=64, dtype="bf16",
+                                   branch="dflash", branch_len=64, anchor_stride=64,
+                                   seed_base=2600),
+    "dspark_b48_bf16": specs.small("b48", (200, 97), hq=8, hkv=2, d=128, dtype="bf16",
+                                   branch="dspark", branch_len=48, anchor_stride=32,
+                                   seed_base=2700),
 }
 
 
@@ -82,6 +112,14 @@ def test_zigzag_ring_small_matches_oracle(cp):
     compare_full(st, t, gpu, TOL["bf16"], f"ring C={cp}")
 
 
+@pytest.mark.parametrize("cp", [3, 4])
+def test_zigzag_ring_mixed_kinds_matches_oracle(cp):
+    w = SMALL["mixed_kinds_bf16"]
+    st, t = inputs(w)
+    gpu = run_path(st, t, cp=cp)
+    compare_full(st, t, gpu, TOL["bf16"], f"mixed ring C={cp}")
+
+
 def test_ring_dflash_matches_unsharded():
     w = SMALL["dflash_bf16"]
     st, t = inputs(w)
@@ -106,7 +144,8 @@ def test_mask_is_bit_exact_with_one_hot_values(impl):
         blens = [int(x) for x in spec["branch_lens"]]
         cu = np.concatenate([[0], np.cumsum(seqlens)])
         per_seq = [[a - cu[s] for a in anchors if cu[s] <= a < cu[s + 1]] for s in range(len(seqlens))]
-        st = make_structure_custom(seqlens, per_seq, blens, spec["kind"][0])
+        kind = spec["kinds"] if "kinds" in spec else spec["kind"][0]
+        st = make_structure_custom(seqlens, per_seq, blens, kind)
         d = 64
         dt = torch.bfloat16 if impl == "bf16" else torch.float32
         n = mat.shape[0]

@@ -25,8 +25,21 @@ class Structure:
     cu_seqlens: np.ndarray      # int32 [S+1]
     branch_cu: np.ndarray       # int32 [A+1]
     branch_anchor: np.ndarray   # int32 [A] global main index of each anchor
-    kind: str                   # 'causal' | 'bidir'
+    kind: str                   # 'causal' | 'bidir' | 'mixed'
     max_branch_len: int
+    branch_kinds: np.ndarray = None   # int32 [A]: 0 causal, 1 bidirectional
+
+    def __post_init__(self):
+        if self.branch_kinds is None:
+            fill = 1 if self.kind == "bidir" else 0
+            self.branch_kinds = np.full(self.branch_anchor.shape[0], fill, dtype=np.int32)
+
+    @property
+    def kind_names(self):
+        """Per-branch kind names (the oracle's form)."""
+        if self.kind in ("causal", "bidir"):
+            return self.kind
+        return ["bidir" if k == 1 else "causal" for k in self.branch_kinds.tolist()]
 
     @property
     def n_main(self) -> int:
@@ -45,16 +58,23 @@ def make_structure(w: Workload) -> Structure:
     lens = np.asarray(w.seqlens, dtype=np.int64)
     cu = np.zeros(len(lens) + 1, dtype=np.int64)
     cu[1:] = np.cumsum(lens)
-    anchors = []
+    rules = w.mix if w.branch == "mixed" else ((w.branch, w.branch_len, w.anchor_stride),) * len(lens)
+    assert len(rules) == len(lens)
+    anchors, blens, kinds = [], [], []
     for s, L in enumerate(lens):
-        anchors.append(cu[s] + np.arange(0, L, w.anchor_stride, dtype=np.int64))
+        fam, blen_s, stride = rules[s]
+        a = cu[s] + np.arange(0, L, stride, dtype=np.int64)
+        anchors.append(a)
+        blens.append(np.full(a.shape[0], blen_s, dtype=np.int64))
+        kinds.append(np.full(a.shape[0], 1 if fam == "dflash" else 0, dtype=np.int32))
     anchor = np.concatenate(anchors) if anchors else np.zeros(0, np.int64)
-    blen = np.full(anchor.shape[0], w.branch_len, dtype=np.int64)
+    blen = np.concatenate(blens) if blens else np.zeros(0, np.int64)
     bcu = np.zeros(anchor.shape[0] + 1, dtype=np.int64)
     bcu[1:] = np.cumsum(blen)
     assert cu[-1] < 2**31 and bcu[-1] < 2**31
     return Structure(cu.astype(np.int32), bcu.astype(np.int32), anchor.astype(np.int32),
-                     w.kind, int(w.branch_len))
+                     w.kind, int(blen.max()) if blen.size else 1,
+                     np.concatenate(kinds) if kinds else np.zeros(0, np.int32))
 
 
 def make_structure_custom(seqlens, anchors_per_seq, branch_lens, kind) -> Structure:
@@ -72,8 +92,12 @@ def make_structure_custom(seqlens, anchors_per_seq, branch_lens, kind) -> Struct
     assert blen.shape[0] == anchor.shape[0]
     bcu = np.zeros(anchor.shape[0] + 1, dtype=np.int64)
     bcu[1:] = np.cumsum(blen)
+    if isinstance(kind, str):
+        return Structure(cu.astype(np.int32), bcu.astype(np.int32), anchor.astype(np.int32),
+                         kind, int(blen.max()) if blen.size else 0)
+    kinds = np.asarray([1 if k == "bidir" else 0 for k in kind], dtype=np.int32)
     return Structure(cu.astype(np.int32), bcu.astype(np.int32), anchor.astype(np.int32),
-                     kind, int(blen.max()) if blen.size else 0)
+                     "mixed", int(blen.max()) if blen.size else 0, kinds)
 
 
 def _torch_dtype(w_dtype: str):

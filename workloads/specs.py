@@ -66,6 +66,7 @@ class Workload:
     tokens every ``anchor_stride`` positions, bidirectional inside) or
     'dspark' (block of B tokens every ``anchor_stride`` positions, causal
     inside).  ``branch_len`` is D or B.
+    'mixed' takes one (family, length, stride) per sequence from ``mix``.
     """
     name: str
     seqlens: Tuple[int, ...]
@@ -82,9 +83,13 @@ class Workload:
     rank: int = 0
     note: str = ""
     extra: dict = field(default_factory=dict, compare=False)
+    # branch == 'mixed': one (family, length, stride) per sequence
+    mix: Tuple[Tuple[str, int, int], ...] = ()
 
     @property
     def kind(self) -> str:
+        if self.branch == "mixed":
+            return "mixed"
         return "bidir" if self.branch == "dflash" else "causal"
 
     @property
@@ -110,6 +115,19 @@ WORKLOADS = {
         Workload("eagle3_256k_rank0_of_8", (262144,), 32, 8, 128, "bf16", "eagle3",
                  3, 1, 1.0, 500, cp=8, rank=0,
                  note="rank 0's share of the 256K sequence under a zigzag ring of 8"),
+        # the 256K scale with the two block-draft families
+        Workload("dflash_256k", (262144,), 32, 8, 128, "bf16", "dflash", 16, 16,
+                 1.0, 600, note="DFlash blocks of 16 every 16 positions, one 262,144-token sequence"),
+        Workload("dspark_256k", (262144,), 32, 8, 128, "bf16", "dspark", 8, 8,
+                 1.0, 700, note="DSpark blocks of 8 every 8 positions, one 262,144-token sequence"),
+        # one varlen pack mixing the three families, one family per sequence
+        Workload("mixed_12k", (4096, 6144, 2048), 32, 8, 128, "bf16", "mixed", 16, 1, 1.0, 800,
+                 note="EAGLE-3 depth 3 / DFlash B=16 / DSpark B=8 in one packed batch",
+                 mix=(("eagle3", 3, 1), ("dflash", 16, 16), ("dspark", 8, 8))),
+        # same length and branch rule as the 256K workload, small enough to
+        # check in full against the oracle (unsharded and under a ring of 8)
+        Workload("eagle3_32k", (32768,), 32, 8, 128, "bf16", "eagle3", 3, 1, 1.0, 900,
+                 note="EAGLE-3 TTT depth 3, one 32,768-token sequence"),
     ]
 }
 
@@ -119,7 +137,7 @@ def get(name: str) -> Workload:
 
 
 def small(name: str, seqlens, hq=4, hkv=2, d=64, dtype="f32", branch="eagle3",
-          branch_len=3, anchor_stride=1, value_scale=1.0, seed_base=900) -> Workload:
+          branch_len=3, anchor_stride=1, value_scale=1.0, seed_base=900, mix=()) -> Workload:
     """A custom small workload for tests (same recipe, other sizes)."""
     return Workload(name, tuple(int(x) for x in seqlens), hq, hkv, d, dtype, branch,
-                    branch_len, anchor_stride, value_scale, seed_base)
+                    branch_len, anchor_stride, value_scale, seed_base, mix=tuple(mix))
