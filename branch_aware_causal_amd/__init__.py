@@ -11,11 +11,12 @@ online-softmax merge, forward and backward, behind the C ABI of libbac.so
 from .api import (BacError, BAC_OK, BAC_EINVAL, BAC_EUNSUPPORTED, BAC_ESIZE, BAC_EHIP, F32, BF16,
                   WRITE, MERGE, CAUSAL, BIDIR, zigzag_shard_plan, attn_main_fwd, attn_branch_fwd,
                   lse_merge, attn_bwd_delta, attn_main_bwd, attn_main_bwd_dq, attn_main_bwd_dkdv,
-                  attn_branch_bwd, attn_check_index)
+                  attn_branch_bwd, attn_check_index, tap_send, tap_recv)
 from . import ring, flops, accounting
 
 __all__ = ["BacError", "BAC_OK", "BAC_EINVAL", "BAC_EUNSUPPORTED", "BAC_ESIZE", "BAC_EHIP",
            "F32", "BF16", "WRITE", "MERGE", "CAUSAL", "BIDIR", "zigzag_shard_plan",
            "attn_main_fwd", "attn_branch_fwd", "lse_merge", "attn_bwd_delta", "attn_main_bwd",
            "attn_main_bwd_dq", "attn_main_bwd_dkdv",
-           "attn_branch_bwd", "attn_check_index", "ring", "flops", "accounting"]
+           "attn_branch_bwd", "attn_check_index", "tap_send", "tap_recv", "ring", "flops",
+           "accounting"]

@@ -48,6 +48,8 @@ SIGNATURES = {
     "attn_branch_bwd": [vp, vp, vp, i32, vp, i32, i32, i32, vp, i32, i32, i32, i32, f32,
                         vp, vp, vp, vp, vp, vp, vp],
     "attn_check_index": [vp, vp, i32, i32, vp, vp],
+    "tap_send": [vp, vp, i32, C.c_int64, i32, vp, C.c_int64, C.c_uint64, vp],
+    "tap_recv": [vp, vp, i32, C.c_int64, i32, C.c_uint64, C.c_int64, vp, C.c_int64, vp, vp],
     "bac_version": [],
 }
 

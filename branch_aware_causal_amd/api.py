@@ -273,3 +273,39 @@ def attn_check_index(seq, pos, strict: bool, stream=None) -> int:
                                       _stream(stream))
     _check(st)
     return int(bad.item())
+
+
+def _mailbox(slots, stamps):
+    torch = _torch()
+    _need(slots, "slots")
+    _need(stamps, "stamps", torch.int64)
+    nslots = slots.shape[0]
+    if stamps.shape != (nslots,):
+        raise ValueError(f"stamps must have shape ({nslots},), got {tuple(stamps.shape)}")
+    return nslots, slots[0].numel() * slots.element_size()
+
+
+def tap_send(slots, stamps, slot: int, payload, seq: int, stream=None):
+    """Copy `payload` into slot `slot` of the mailbox (slots [nslots, ...],
+    stamps int64 [nslots]) and publish stamps[slot] = seq (include/bac.h)."""
+    nslots, slot_bytes = _mailbox(slots, stamps)
+    _need(payload, "payload")
+    st = _lib.load().tap_send(_ptr(slots), _ptr(stamps), nslots, slot_bytes, int(slot),
+                              _ptr(payload), payload.numel() * payload.element_size(), int(seq),
+                              _stream(stream))
+    _check(st)
+
+
+def tap_recv(slots, stamps, slot: int, seq: int, out, status, spin_limit: int = 1 << 22,
+             stream=None):
+    """Wait (at most spin_limit polls) for stamps[slot] == seq, then copy the
+    slot into `out`; status (int32 [1], device) receives 0 received, 1 gave
+    up, 2 the slot holds a newer sequence."""
+    torch = _torch()
+    nslots, slot_bytes = _mailbox(slots, stamps)
+    _need(out, "out")
+    _need(status, "status", torch.int32, (1,))
+    st = _lib.load().tap_recv(_ptr(slots), _ptr(stamps), nslots, slot_bytes, int(slot), int(seq),
+                              int(spin_limit), _ptr(out), out.numel() * out.element_size(),
+                              _ptr(status), _stream(stream))
+    _check(st)

@@ -24,6 +24,7 @@ SOURCES = [
     "valu_attention.hip",
     "mfma_fwd.hip",
     "mfma_bwd.hip",
+    "tapchannel.hip",
 ]
 
 # -packed-fp32-ops keeps hipcc from emitting packed fp32 VALU instructions.
@@ -41,9 +42,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: install ROCm or set HIPCC")
 
 
+# Per-source extra hipcc flags.
+EXTRA_FLAGS: dict = {}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+           "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

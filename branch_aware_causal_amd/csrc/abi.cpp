@@ -295,4 +295,51 @@ bac_status attn_check_index(const int32_t* seq, const int32_t* pos, int32_t n, i
                     fn);
 }
 
+static bac_status check_mailbox(const char* fn, const void* slots, const void* stamps,
+                                int32_t nslots, int64_t slot_bytes, int32_t slot, int64_t nbytes,
+                                uint64_t seq, const void* buf) {
+  if (!slots || !stamps || (nbytes > 0 && !buf))
+    return fail(BAC_EINVAL, "%s: null slots, stamps or buffer", fn);
+  if (nslots < 1 || slot < 0 || slot >= nslots)
+    return fail(BAC_EINVAL, "%s: slot %d outside [0, %d)", fn, slot, nslots);
+  if (slot_bytes < 16 || slot_bytes % 16 != 0)
+    return fail(BAC_EINVAL, "%s: slot_bytes %lld is not a positive multiple of 16", fn,
+                static_cast<long long>(slot_bytes));
+  if (nbytes < 0 || nbytes > slot_bytes)
+    return fail(BAC_EINVAL, "%s: nbytes %lld outside [0, slot_bytes]", fn,
+                static_cast<long long>(nbytes));
+  if (seq == 0) return fail(BAC_EINVAL, "%s: sequence numbers start at 1", fn);
+  BAC_TRY(check_aligned(fn, {slots, buf}));
+  if (reinterpret_cast<uintptr_t>(stamps) & 7u)
+    return fail(BAC_EINVAL, "%s: stamps are not 8-byte aligned", fn);
+  return BAC_OK;
+}
+
+bac_status tap_send(void* slots, uint64_t* stamps, int32_t nslots, int64_t slot_bytes,
+                    int32_t slot, const void* payload, int64_t nbytes, uint64_t seq,
+                    void* stream) {
+  clear_error();
+  const char* fn = "tap_send";
+  BAC_TRY(check_mailbox(fn, slots, stamps, nslots, slot_bytes, slot, nbytes, seq, payload));
+  char* dst = static_cast<char*>(slots) + static_cast<int64_t>(slot) * slot_bytes;
+  return hip_status(launch_tap_send(dst, stamps, slot, payload, nbytes, seq,
+                                    static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+bac_status tap_recv(const void* slots, const uint64_t* stamps, int32_t nslots,
+                    int64_t slot_bytes, int32_t slot, uint64_t seq, int64_t spin_limit,
+                    void* out, int64_t nbytes, int32_t* status, void* stream) {
+  clear_error();
+  const char* fn = "tap_recv";
+  BAC_TRY(check_mailbox(fn, slots, stamps, nslots, slot_bytes, slot, nbytes, seq, out));
+  if (!status) return fail(BAC_EINVAL, "%s: null status", fn);
+  if (spin_limit < 1) return fail(BAC_EINVAL, "%s: spin_limit %lld < 1", fn,
+                                  static_cast<long long>(spin_limit));
+  const char* src = static_cast<const char*>(slots) + static_cast<int64_t>(slot) * slot_bytes;
+  return hip_status(launch_tap_recv(src, stamps, slot, seq, spin_limit, out, nbytes, status,
+                                    static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 }  // extern "C"

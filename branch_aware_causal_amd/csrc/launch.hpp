@@ -75,6 +75,11 @@ hipError_t launch_lse_merge(float* o_acc, float* lse_acc, const float* o_part, c
                             int n, int hq, int d, int out_dt, void* o_out, hipStream_t s);
 hipError_t launch_delta(const void* o, int o_dt, const void* dout, int dt, int n, int hq, int d,
                         float* delta, hipStream_t s);
+hipError_t launch_tap_send(void* slot_ptr, uint64_t* stamps, int slot, const void* payload,
+                           int64_t nbytes, uint64_t seq, hipStream_t s);
+hipError_t launch_tap_recv(const void* slot_ptr, const uint64_t* stamps, int slot, uint64_t seq,
+                           int64_t spin_limit, void* out, int64_t nbytes, int32_t* status,
+                           hipStream_t s);
 hipError_t launch_check_index(const int32_t* seq, const int32_t* pos, int n, int strict,
                               int32_t* bad, hipStream_t s);
 

@@ -260,6 +260,42 @@ bac_status attn_branch_bwd(const void* qb, const void* kb, const void* vb, int32
 bac_status attn_check_index(const int32_t* seq, const int32_t* pos, int32_t n, int32_t strict,
                             int32_t* bad_count, void* stream);
 
+/* ------------------------------------------------------------------------
+ * tap_send / tap_recv -- one-way hand-off of a feature buffer through
+ * preallocated device slots with sequence stamps, off any pipeline schedule
+ * ([G] 技术贡献 and 方法详解 · PP传输: producers write target features into
+ * the consumer's preallocated slots and bump a sequence stamp; the consumer
+ * reads by stamp).  Single-device form: producer and consumer are streams
+ * of one GPU.
+ *
+ * Mailbox (device, caller-owned): slots = nslots slots of slot_bytes bytes
+ * each (slot_bytes a multiple of 16; slots 16-byte aligned); stamps =
+ * nslots uint64 sequence stamps, zeroed by the caller before first use
+ * (0 = nothing sent yet).  Sequence numbers are >= 1.
+ *
+ * tap_send: copies nbytes (<= slot_bytes) of payload (device, 16-byte
+ *   aligned) into slot `slot`, then stores stamps[slot] = seq with release
+ *   semantics: a consumer that sees the stamp sees the whole payload.  Both
+ *   steps are enqueued on `stream`.  The caller does not reuse a slot while
+ *   a consumer of its previous contents may still be reading it.
+ * tap_recv: enqueued on `stream`; waits until stamps[slot] >= seq, polling
+ *   at most spin_limit (>= 1) times per workgroup with a short sleep between
+ *   polls, then copies nbytes of the slot to out (device, 16-byte aligned)
+ *   if the stamp equals seq.  *status (device int32, overwritten):
+ *   0 = received; 1 = gave up (the stamp stayed below seq for spin_limit
+ *   polls; out is not fully written); 2 = the slot already holds a newer
+ *   sequence.  The wait never outlasts its spin limit.
+ * Errors: BAC_EINVAL for null pointers, slot outside [0, nslots), nbytes
+ *   outside [0, slot_bytes], slot_bytes not a multiple of 16, misaligned
+ *   buffers, seq == 0 or spin_limit < 1.
+ * ---------------------------------------------------------------------- */
+bac_status tap_send(void* slots, uint64_t* stamps, int32_t nslots, int64_t slot_bytes,
+                    int32_t slot, const void* payload, int64_t nbytes, uint64_t seq,
+                    void* stream);
+bac_status tap_recv(const void* slots, const uint64_t* stamps, int32_t nslots,
+                    int64_t slot_bytes, int32_t slot, uint64_t seq, int64_t spin_limit,
+                    void* out, int64_t nbytes, int32_t* status, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

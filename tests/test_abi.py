@@ -192,3 +192,35 @@ def test_plan_matches_hand_computed_fixtures():
             got = zigzag_shard_plan(cu, bcu, anchors, C_, r)
             for key in PLAN_KEYS:
                 assert np.array_equal(got[key], want[key].astype(np.int32)), (fname, r, key)
+
+
+@pytest.mark.parametrize("over,needle", [
+    (dict(slots=None), "null"),
+    (dict(slot=2), "outside"),
+    (dict(slot=-1), "outside"),
+    (dict(nbytes=4097), "outside [0, slot_bytes]"),
+    (dict(slot_bytes=100), "multiple of 16"),
+    (dict(seq=0), "start at 1"),
+    (dict(buf=8), "16-byte aligned"),
+    (dict(stamps=12), "8-byte aligned"),
+])
+def test_mailbox_calls_reject_bad_arguments(lib, over, needle):
+    from branch_aware_causal_amd import _lib
+    a = dict(slots=256, stamps=16, nslots=2, slot_bytes=4096, slot=1, buf=512, nbytes=4096, seq=3)
+    a.update(over)
+    vp = C.c_void_p
+    st = lib.tap_send(vp(a["slots"]), vp(a["stamps"]), a["nslots"], a["slot_bytes"], a["slot"],
+                      vp(a["buf"]), a["nbytes"], a["seq"], vp(None))
+    assert st == -1 and needle in _lib.last_error(), _lib.last_error()
+    st = lib.tap_recv(vp(a["slots"]), vp(a["stamps"]), a["nslots"], a["slot_bytes"], a["slot"],
+                      a["seq"], 100, vp(a["buf"]), a["nbytes"], vp(64), vp(None))
+    assert st == -1 and needle in _lib.last_error(), _lib.last_error()
+
+
+def test_mailbox_recv_rejects_bad_wait_arguments(lib):
+    from branch_aware_causal_amd import _lib
+    vp = C.c_void_p
+    st = lib.tap_recv(vp(256), vp(16), 2, 4096, 1, 3, 0, vp(512), 4096, vp(64), vp(None))
+    assert st == -1 and "spin_limit" in _lib.last_error()
+    st = lib.tap_recv(vp(256), vp(16), 2, 4096, 1, 3, 10, vp(512), 4096, vp(None), vp(None))
+    assert st == -1 and "status" in _lib.last_error()
