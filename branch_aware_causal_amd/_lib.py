@@ -61,7 +61,8 @@ def load(path: str | None = None):
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    # BAC_LIB names another build of the same ABI (e.g. a sanitizer build)
+    p = path or os.environ.get("BAC_LIB") or LIB_PATH
     if not os.path.exists(p):
         raise ImportError(
             f"{p} is missing: build it with `python -m branch_aware_causal_amd.build` "
