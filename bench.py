@@ -234,7 +234,7 @@ def traffic_for(kernel, workload):
         return None
 
 
-def cpu_baseline(w, st, t, n_anchor, log_fn):
+def cpu_baseline(w, st, t, n_anchor, log_fn, full_flops):
     """The oracle, timed on the host on the rows of the last n_anchor anchors
     (their main rows and every token of their branches), each row over its full
     visible key set, all heads: O, lse and the gradients of the block."""
@@ -281,8 +281,13 @@ def cpu_baseline(w, st, t, n_anchor, log_fn):
     oracle.backward_rows(prob, rows, dO)
     dt = time.perf_counter() - t0
     flop = pairs * 14 * w.d
-    log_fn(f"cpu_baseline: {rows.size} rows, {pairs:,} (row, key, head) triples, {dt:.1f} s")
-    return dict(value=flop / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+    rate = flop / dt
+    log_fn(f"cpu_baseline: {rows.size} rows, {pairs:,} (row, key, head) triples, {dt:.1f} s; "
+           f"whole step extrapolated at this rate: {full_flops / rate / 3600:.1f} h")
+    return dict(value=rate / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+                extrapolated_full_step_s=round(full_flops / rate, 1),
+                extrapolated_note=("EXTRAPOLATED, not measured: the whole step's algorithmic "
+                                   "FLOP divided by the sampled oracle rate"),
                 sample=(f"fp64 NumPy oracle, fwd+bwd (O, lse, dQ and the block's dK/dV) of the "
                         f"rows of the last {n_anchor} anchors of the {w.name} workload "
                         f"({main_rows.size} main + {br_tok.size} branch rows over ~{N:,} keys, "
@@ -399,7 +404,7 @@ def main():
     cpu = None
     if args.cpu_anchors > 0:
         try:
-            cpu = cpu_baseline(w, st, t, args.cpu_anchors, log)
+            cpu = cpu_baseline(w, st, t, args.cpu_anchors, log, work["flops"])
         except Exception as e:  # report, keep the GPU result
             log(f"cpu_baseline failed: {e!r}")
 
