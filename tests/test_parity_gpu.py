@@ -67,6 +67,11 @@ SMALL = {
                                          branch="eagle3", branch_len=3, seed_base=2200),
     "eagle3_gqa32_d128_bf16": specs.small("q32b", (150, 9), hq=32, hkv=1, d=128, dtype="bf16",
                                           branch="eagle3", branch_len=2, seed_base=2300),
+    # empty sequences inside a pack (their ids own no token) and a sequence
+    # shorter than one DSpark block
+    "dspark_empty_seqs_bf16": specs.small("e0", (120, 0, 64, 0, 7), hq=8, hkv=2, d=128,
+                                          dtype="bf16", branch="dspark", branch_len=8,
+                                          anchor_stride=8, seed_base=2800),
     # one pack mixing the three families, each branch with its own kind
     "mixed_kinds_bf16": specs.small("mix", (150, 96, 40), hq=8, hkv=2, d=128, dtype="bf16",
                                     branch="mixed", seed_base=2400,
@@ -118,6 +123,14 @@ def test_zigzag_ring_mixed_kinds_matches_oracle(cp):
     st, t = inputs(w)
     gpu = run_path(st, t, cp=cp)
     compare_full(st, t, gpu, TOL["bf16"], f"mixed ring C={cp}")
+
+
+@pytest.mark.parametrize("cp", [2, 3])
+def test_zigzag_ring_with_empty_sequences_matches_oracle(cp):
+    w = SMALL["dspark_empty_seqs_bf16"]
+    st, t = inputs(w)
+    gpu = run_path(st, t, cp=cp)
+    compare_full(st, t, gpu, TOL["bf16"], f"empty-sequence ring C={cp}")
 
 
 def test_ring_dflash_matches_unsharded():
