@@ -136,12 +136,12 @@ __device__ __forceinline__ float group_sum(float x) {
 // ---------------------------------------------------------------------------
 // Branch forward: wave w of block b handles branch a = 4b + w, kv-head
 // blockIdx.y, i.e. rows (t, h) for every token t of the branch and every
-// q-head h of the group.  A row occupies D/8 lanes (eight elements each, so
+// q-head h of the group, TB tokens at a time.  A row occupies D/8 lanes (eight elements each, so
 // every access is 16 or 32 contiguous bytes per lane) and a pass covers
 // 64/(D/8) q-heads of the group at once; dot products are DPP sums inside
 // each row's lanes.  No LDS; tokens past max_len are left untouched.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, int TB>
 __global__ __launch_bounds__(256) void branch_fwd_kernel(const T* __restrict__ qb,
                                                          const T* __restrict__ kb,
                                                          const T* __restrict__ vb, int nb,
@@ -163,55 +163,74 @@ __global__ __launch_bounds__(256) void branch_fwd_kernel(const T* __restrict__ q
   const int t0 = max(0, min(bcu[a], nb));
   const int t1 = max(t0, min(bcu[a + 1], nb));
   const int len = min(t1 - t0, max_len);   // tokens past the bound are left untouched
+  // TB tokens per step: each K/V row loaded serves TB rows (the per-row
+  // online-softmax updates run in the same key order as one token at a time)
   for (int c0 = 0; c0 < G; c0 += RPW) {
     // lanes past the group's last q-head repeat its first and store nothing
     const bool row_ok = c0 + r < G;
     const int h = g * G + (row_ok ? c0 + r : 0);
-    for (int t = 0; t < len; ++t) {
-      const int kend = bidir ? len : t + 1;
-      const size_t qoff = (static_cast<size_t>(t0 + t) * hq + h) * D + col;
-      float q[8], o[8];
-      load8<T>(qb, qoff, q);
+    for (int tb = 0; tb < len; tb += TB) {
+      const int nt = min(TB, len - tb);
+      float q[TB][8], o[TB][8], m2[TB], l[TB];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = 0.f;
-      float m2 = kNegInf, l = 0.f;
+      for (int j = 0; j < TB; ++j) {
+        // slots past the last token repeat it; their results are dropped
+        const int t = tb + min(j, nt - 1);
+        load8<T>(qb, (static_cast<size_t>(t0 + t) * hq + h) * D + col, q[j]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+        m2[j] = kNegInf;
+        l[j] = 0.f;
+      }
+      const int kend = bidir ? len : tb + nt;   // keys some token of the step sees
       for (int u = 0; u < kend; ++u) {
         const size_t koff = (static_cast<size_t>(t0 + u) * hkv + g) * D + col;
         float kk[8], vv[8];
         load8<T>(kb, koff, kk);
         load8<T>(vb, koff, vv);
-        float dot = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dot = fmaf(q[e], kk[e], dot);
-        dot = group_sum<LPR>(dot);
-        online_update<8>(dot * scale_log2, vv, m2, l, o);
+        for (int j = 0; j < TB; ++j) {
+          if (j < nt && (bidir || u <= tb + j)) {   // wave-uniform
+            float dot = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dot = fmaf(q[j][e], kk[e], dot);
+            dot = group_sum<LPR>(dot);
+            online_update<8>(dot * scale_log2, vv, m2[j], l[j], o[j]);
+          }
+        }
       }
       if (!row_ok) continue;
-      // normalise, merge into the accumulators if asked, store
-      float lse2, inv;
-      if (l > 0.f) {
-        lse2 = m2 + log2_fast(l);
-        inv = 1.f / l;
-      } else {
-        lse2 = kNegInf;
-        inv = 0.f;
-      }
-      const size_t lidx = static_cast<size_t>(h) * nb + t0 + t;
-      float res[8];
-      float lnew = lse2;
-      if (mode == 1) {
-        float wa, wb, prev[8];
-        merge_weights_log2(lse_acc[lidx] * kLog2e, lse2, wa, wb, lnew);
-        load8<float>(o_acc, qoff, prev);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) res[e] = wa * prev[e] + wb * (o[e] * inv);
-      } else {
+      for (int j = 0; j < TB; ++j) {
+        if (j >= nt) break;
+        const int t = tb + j;
+        const size_t qoff = (static_cast<size_t>(t0 + t) * hq + h) * D + col;
+        // normalise, merge into the accumulators if asked, store
+        float lse2, inv;
+        if (l[j] > 0.f) {
+          lse2 = m2[j] + log2_fast(l[j]);
+          inv = 1.f / l[j];
+        } else {
+          lse2 = kNegInf;
+          inv = 0.f;
+        }
+        const size_t lidx = static_cast<size_t>(h) * nb + t0 + t;
+        float res[8];
+        float lnew = lse2;
+        if (mode == 1) {
+          float wa, wb, prev[8];
+          merge_weights_log2(lse_acc[lidx] * kLog2e, lse2, wa, wb, lnew);
+          load8<float>(o_acc, qoff, prev);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) res[e] = o[e] * inv;
+          for (int e = 0; e < 8; ++e) res[e] = wa * prev[e] + wb * (o[j][e] * inv);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) res[e] = o[j][e] * inv;
+        }
+        store8<float>(o_acc, qoff, res);
+        if (o_out) store8<T>(o_out, qoff, res);
+        if (col == 0) lse_acc[lidx] = (lnew == kNegInf) ? kNegInf : lnew * kLn2;
       }
-      store8<float>(o_acc, qoff, res);
-      if (o_out) store8<T>(o_out, qoff, res);
-      if (col == 0) lse_acc[lidx] = (lnew == kNegInf) ? kNegInf : lnew * kLn2;
     }
   }
 }
@@ -221,14 +240,18 @@ __global__ __launch_bounds__(256) void branch_fwd_kernel(const T* __restrict__ q
 // forward (D/8 lanes per row, 64/(D/8) q-heads per pass).  For a row (t, h)
 // and a visible key u: s = <q, k_u>, P = exp2(s*c - lse2), dP = <dO, v_u>,
 // dS = P (dP - Delta).  Two passes, both recomputing s and dP:
-//   1. token-outer: dq_row += dS k_u in registers, one += per row;
-//   2. key-outer: dk_u += dS q_row, dv_u += P dO_row in registers over every
-//      row that sees u, then summed over the pass's q-heads (shuffles across
-//      the row groups) and added once per key.
+//   1. token-outer, TB tokens per step: dq_row += dS k_u in registers, one
+//      += per row;
+//   2. key-outer, KB keys per step: dk_u += dS q_row, dv_u += P dO_row in
+//      registers over every row that sees u, then summed over the pass's
+//      q-heads (shuffles across the row groups) and added once per key.
+// Each K/V row loaded in pass 1 serves TB rows and each Q/dO row loaded in
+// pass 2 serves KB keys; every row and key still sums its terms in the same
+// order as one at a time.
 // The wave owns every row and key it touches, so += on the global
 // accumulators is race-free and no LDS is needed.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, int TB, int KB>
 __global__ __launch_bounds__(256) void branch_bwd_kernel(
     const T* __restrict__ qb, const T* __restrict__ kb, const T* __restrict__ vb, int nb,
     const int32_t* __restrict__ bcu, int A, int max_len, int bidir_all,
@@ -262,85 +285,122 @@ __global__ __launch_bounds__(256) void branch_bwd_kernel(
     p = (lse2 == kNegInf) ? 0.f : exp2_fast(s * scale_log2 - lse2);
     ds = p * (dp - dl);
   };
-  // pass 1: dQ
+  // pass 1: dQ, TB tokens per step (each K/V row loaded serves TB rows; every
+  // row sums its keys in the same order as one token at a time)
   for (int c0 = 0; c0 < G; c0 += RPW) {
     const bool row_ok = c0 + r < G;
     const int h = g * G + (row_ok ? c0 + r : 0);
-    for (int t = 0; t < len; ++t) {
-      const int kend = bidir ? len : t + 1;
-      const size_t qoff = (static_cast<size_t>(t0 + t) * hq + h) * D + col;
-      const size_t li = static_cast<size_t>(h) * nb + t0 + t;
-      float q[8], d_o[8], dqr[8];
-      load8<T>(qb, qoff, q);
-      load8<T>(dout, qoff, d_o);
-      const float lse2 = lse[li] * kLog2e, dl = delta[li];
+    for (int tb = 0; tb < len; tb += TB) {
+      const int nt = min(TB, len - tb);
+      float q[TB][8], d_o[TB][8], dqr[TB][8], lse2[TB], dl[TB];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dqr[e] = 0.f;
+      for (int j = 0; j < TB; ++j) {
+        // slots past the last token repeat it; their results are dropped
+        const int t = tb + min(j, nt - 1);
+        const size_t qoff = (static_cast<size_t>(t0 + t) * hq + h) * D + col;
+        const size_t li = static_cast<size_t>(h) * nb + t0 + t;
+        load8<T>(qb, qoff, q[j]);
+        load8<T>(dout, qoff, d_o[j]);
+        lse2[j] = lse[li] * kLog2e;
+        dl[j] = delta[li];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dqr[j][e] = 0.f;
+      }
+      const int kend = bidir ? len : tb + nt;   // keys some token of the step sees
       for (int u = 0; u < kend; ++u) {
         const size_t koff = (static_cast<size_t>(t0 + u) * hkv + g) * D + col;
-        float kk[8], vv[8], p, ds;
+        float kk[8], vv[8];
         load8<T>(kb, koff, kk);
         load8<T>(vb, koff, vv);
-        p_ds(q, d_o, lse2, dl, kk, vv, p, ds);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dqr[e] = fmaf(ds, kk[e], dqr[e]);
+        for (int j = 0; j < TB; ++j) {
+          if (j < nt && (bidir || u <= tb + j)) {   // wave-uniform
+            float p, ds;
+            p_ds(q[j], d_o[j], lse2[j], dl[j], kk, vv, p, ds);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dqr[j][e] = fmaf(ds, kk[e], dqr[j][e]);
+          }
+        }
       }
       if (!row_ok) continue;
-      float cur[8];
-      load8<float>(dq, qoff, cur);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) cur[e] = fmaf(scale, dqr[e], cur[e]);
-      store8<float>(dq, qoff, cur);
+      for (int j = 0; j < TB; ++j) {
+        if (j >= nt) break;
+        const size_t qoff = (static_cast<size_t>(t0 + tb + j) * hq + h) * D + col;
+        float cur[8];
+        load8<float>(dq, qoff, cur);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cur[e] = fmaf(scale, dqr[j][e], cur[e]);
+        store8<float>(dq, qoff, cur);
+      }
     }
   }
-  // pass 2: dK, dV
-  for (int u = 0; u < len; ++u) {
-    const size_t koff = (static_cast<size_t>(t0 + u) * hkv + g) * D + col;
-    float kk[8], vv[8], dka[8], dva[8];
-    load8<T>(kb, koff, kk);
-    load8<T>(vb, koff, vv);
+  // pass 2: dK, dV, KB keys per step (each Q/dO row loaded serves KB keys;
+  // every key sums its rows in the same order as one key at a time)
+  for (int ub = 0; ub < len; ub += KB) {
+    const int nk = min(KB, len - ub);
+    float kk[KB][8], vv[KB][8], dka[KB][8], dva[KB][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      dka[e] = 0.f;
-      dva[e] = 0.f;
+    for (int i = 0; i < KB; ++i) {
+      const size_t koff = (static_cast<size_t>(t0 + ub + min(i, nk - 1)) * hkv + g) * D + col;
+      load8<T>(kb, koff, kk[i]);
+      load8<T>(vb, koff, vv[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dka[i][e] = 0.f;
+        dva[i][e] = 0.f;
+      }
     }
     for (int c0 = 0; c0 < G; c0 += RPW) {
       const bool row_ok = c0 + r < G;
       const int h = g * G + (row_ok ? c0 + r : 0);
-      for (int t = bidir ? 0 : u; t < len; ++t) {
+      for (int t = bidir ? 0 : ub; t < len; ++t) {   // rows some key of the step is seen by
         const size_t qoff = (static_cast<size_t>(t0 + t) * hq + h) * D + col;
         const size_t li = static_cast<size_t>(h) * nb + t0 + t;
-        float q[8], d_o[8], p, ds;
+        float q[8], d_o[8];
         load8<T>(qb, qoff, q);
         load8<T>(dout, qoff, d_o);
-        p_ds(q, d_o, lse[li] * kLog2e, delta[li], kk, vv, p, ds);
-        if (!row_ok) continue;
+        const float lse2 = lse[li] * kLog2e, dl = delta[li];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          dka[e] = fmaf(ds, q[e], dka[e]);
-          dva[e] = fmaf(p, d_o[e], dva[e]);
+        for (int i = 0; i < KB; ++i) {
+          if (i < nk && (bidir || t >= ub + i)) {   // wave-uniform
+            float p, ds;
+            p_ds(q, d_o, lse2, dl, kk[i], vv[i], p, ds);
+            if (row_ok) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                dka[i][e] = fmaf(ds, q[e], dka[i][e]);
+                dva[i][e] = fmaf(p, d_o[e], dva[i][e]);
+              }
+            }
+          }
         }
       }
     }
-    // sum over the row groups (lanes that differ by multiples of LPR)
 #pragma unroll
-    for (int off = LPR; off < 64; off <<= 1)
+    for (int i = 0; i < KB; ++i) {
+      if (i >= nk) break;
+      // sum over the row groups (lanes that differ by multiples of LPR)
+#pragma unroll
+      for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          dka[i][e] += __shfl_xor(dka[i][e], off);
+          dva[i][e] += __shfl_xor(dva[i][e], off);
+        }
+      if (r != 0) continue;
+      const size_t koff = (static_cast<size_t>(t0 + ub + i) * hkv + g) * D + col;
+      float ck[8], cv[8];
+      load8<float>(dk, koff, ck);
+      load8<float>(dv, koff, cv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        dka[e] += __shfl_xor(dka[e], off);
-        dva[e] += __shfl_xor(dva[e], off);
+        ck[e] = fmaf(scale, dka[i][e], ck[e]);
+        cv[e] += dva[i][e];
       }
-    if (r != 0) continue;
-    float ck[8], cv[8];
-    load8<float>(dk, koff, ck);
-    load8<float>(dv, koff, cv);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      ck[e] = fmaf(scale, dka[e], ck[e]);
-      cv[e] += dva[e];
+      store8<float>(dk, koff, ck);
+      store8<float>(dv, koff, cv);
     }
-    store8<float>(dk, koff, ck);
-    store8<float>(dv, koff, cv);
   }
 }
 
@@ -455,7 +515,11 @@ __global__ __launch_bounds__(256) void branch_bwd_short_kernel(
 template <typename T, int D>
 static void branch_fwd_d(const BranchArgs& a) {
   const dim3 grid((a.num_branches + 3) / 4, a.hkv);
-  hipLaunchKernelGGL((branch_fwd_kernel<T, D>), grid, dim3(256), 0, a.stream,
+  // branches of at most 4 tokens one token per step (more registers would
+  // cost occupancy for little reuse), longer ones four (measured on 16-token
+  // DFlash blocks: 4 beat 2 and 8)
+  auto kern = a.max_len <= 4 ? branch_fwd_kernel<T, D, 1> : branch_fwd_kernel<T, D, 4>;
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, a.stream,
                      static_cast<const T*>(a.qb), static_cast<const T*>(a.kb),
                      static_cast<const T*>(a.vb), a.nb, a.branch_cu, a.num_branches, a.max_len,
                      a.bidir, a.kinds, a.hq, a.hkv, a.scale * kLog2e, a.o_acc, a.lse_acc, a.mode,
@@ -485,7 +549,10 @@ static void branch_bwd_d(const BranchArgs& a) {
                        a.delta, a.dq, a.dk, a.dv);
     return;
   }
-  hipLaunchKernelGGL((branch_bwd_kernel<T, D>), grid, dim3(256), 0, a.stream,
+  // two tokens per step in the dQ pass and two keys per step in the dK/dV
+  // pass (measured on 8- and 16-token blocks: 4 keys cost more occupancy
+  // than they save)
+  hipLaunchKernelGGL((branch_bwd_kernel<T, D, 2, 2>), grid, dim3(256), 0, a.stream,
                      static_cast<const T*>(a.qb), static_cast<const T*>(a.kb),
                      static_cast<const T*>(a.vb), a.nb, a.branch_cu, a.num_branches, a.max_len,
                      a.bidir, a.kinds, a.hq, a.hkv, a.scale, static_cast<const T*>(a.dout), a.lse,
