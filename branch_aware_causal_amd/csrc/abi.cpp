@@ -122,7 +122,7 @@ extern "C" {
 
 const char* bac_last_error(void) { return g_error.c_str(); }
 
-int32_t bac_version(void) { return 100; }
+int32_t bac_version(void) { return 200; }   // 0.2.0: per-branch kinds, tap_send / tap_recv
 
 bac_status attn_main_fwd(const void* q, const int32_t* q_seq, const int32_t* q_pos, int32_t nq,
                          const void* k, const void* v, const int32_t* k_seq, const int32_t* k_pos,

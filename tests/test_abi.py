@@ -38,6 +38,13 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_version_matches_the_header_generation(lib):
+    # 0.2.0 added the per-branch kind array of the branch calls and the
+    # feature hand-off pair
+    assert lib.bac_version() == 200
+    assert {"tap_send", "tap_recv"} <= set(header_functions())
+
+
 def test_binding_has_the_same_names():
     import branch_aware_causal_amd as bac
     for n in header_functions():
