@@ -297,7 +297,7 @@ def cpu_baseline(w, st, t, n_anchor, log_fn, full_flops):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="eagle3_256k")
     ap.add_argument("--cpu-anchors", type=int, default=16,
