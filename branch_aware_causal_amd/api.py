@@ -126,8 +126,11 @@ def attn_main_fwd(q, q_seq, q_pos, k, v, k_seq, k_pos, o_acc, lse, mode="write",
     _check(st)
 
 
-def _branch_kinds(branch_kinds, A):
-    """Per-branch kinds (device int32 [A], or None for one kind for all)."""
+def _branch_kinds(kind, branch_kinds, A):
+    """Per-branch kinds (device int32 [A], or None for one kind for all);
+    kind "mixed" requires them."""
+    if kind == "mixed" and branch_kinds is None:
+        raise ValueError('kind "mixed" needs branch_kinds (int32, one per branch)')
     if branch_kinds is not None:
         _need(branch_kinds, "branch_kinds", _torch().int32, (A,))
     return _ptr(branch_kinds)
@@ -144,7 +147,7 @@ def attn_branch_fwd(qb, kb, vb, branch_cu, max_branch_len, kind, o_acc, lse, mod
     _need(vb, "vb", qb.dtype, (nb, hkv, d))
     _need(branch_cu, "branch_cu", torch.int32)
     A = branch_cu.shape[0] - 1
-    kinds = _branch_kinds(branch_kinds, A)
+    kinds = _branch_kinds(kind, branch_kinds, A)
     _need(o_acc, "o_acc", torch.float32, (nb, hq, d))
     _need(lse, "lse", torch.float32, (hq, nb))
     if o_out is not None:
@@ -254,7 +257,7 @@ def attn_branch_bwd(qb, kb, vb, branch_cu, max_branch_len, kind, doutb, lseb, de
     _need(dqb, "dqb", torch.float32, (nb, hq, d))
     _need(dkb, "dkb", torch.float32, (nb, hkv, d))
     _need(dvb, "dvb", torch.float32, (nb, hkv, d))
-    kinds = _branch_kinds(branch_kinds, A)
+    kinds = _branch_kinds(kind, branch_kinds, A)
     st = _lib.load().attn_branch_bwd(_ptr(qb), _ptr(kb), _ptr(vb), nb, _ptr(branch_cu), A,
                                      int(max_branch_len), _KINDS[kind], kinds, hq, hkv, d, dt,
                                      _scale(scale, d), _ptr(doutb), _ptr(lseb), _ptr(deltab),

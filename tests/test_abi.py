@@ -45,6 +45,13 @@ def test_version_matches_the_header_generation(lib):
     assert {"tap_send", "tap_recv"} <= set(header_functions())
 
 
+def test_binding_rejects_mixed_kind_without_per_branch_kinds():
+    from branch_aware_causal_amd import api
+    with pytest.raises(ValueError, match="mixed"):
+        api._branch_kinds("mixed", None, 3)
+    assert api._branch_kinds("causal", None, 3).value is None
+
+
 def test_binding_has_the_same_names():
     import branch_aware_causal_amd as bac
     for n in header_functions():
