@@ -359,33 +359,38 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
 //   * consumer (waves 4-7): dV^T += dO^T P and dK^T += Q^T dS for the group
 //     over the tile's rows, both operands by transposing LDS reads, the
 //     accumulators in registers for the whole block.
-// Two barriers per tile.  Half-step 1 of iteration i: the producer runs the
-// S / dP MFMAs of tile i while the consumer reads the P / dS tiles of tile
-// i-1 into registers; half-step 2: the producer's softmax gradient of tile i
-// (vector ALUs) overlaps the consumer's dV / dK MFMAs of tile i-1 on the
-// same SIMD.  Q / dO tiles and their rows' lse, Delta, seq, pos come by
-// direct global->LDS loads, issued by the consumer waves in half-step 1
-// (where they only read the exchange tiles), into a four-stage ring: tile
-// i+2 is loaded in iteration i into the stage of tile i-2 (whose last
-// reader, the consumer's tile i-2, finished in iteration i-1), and each
-// consumer waits for its loads of tile i+1 at the barrier that opens
-// iteration i+1, keeping only its newest batch in flight.  Past the last
-// tile the loads repeat the last tile into a stage no later iteration
-// reads.  The producer reads a tile's row meta before its MFMAs and decides
-// afterwards whether the group sees the tile.
+// One barrier per tile.  In iteration i the producer runs the S / dP MFMAs
+// of tile i and then its softmax gradient (vector ALUs), writing the P / dS
+// tiles of tile i into exchange buffer i % 2; the consumer issues the loads
+// of tile i+2, reads the P / dS tiles of tile i-1 from the other buffer and
+// runs its dV / dK MFMAs of tile i-1.  The two waves of a SIMD interleave
+// freely between barriers.  (Two barriers per tile, splitting the iteration
+// into an MFMA half-step and a softmax half-step, cost 6% more time at 256K:
+// the second barrier's wait outweighed the pairing it enforced.)  Q / dO
+// tiles and their rows' lse, Delta, seq, pos come by direct global->LDS
+// loads, issued by the consumer waves, into a four-stage ring: tile i+2 is
+// loaded in iteration i into the stage of tile i-2 (whose last readers, the
+// producer in iteration i-2 and the consumer in iteration i-1, finished
+// before the barrier that opened iteration i), and each consumer waits for
+// its loads of tile i+1 at the barrier that opens iteration i+1, keeping
+// only its newest batch in flight.  Past the last tile the loads repeat the
+// last tile into a stage no later iteration reads.  The producer reads a
+// tile's row meta before its MFMAs and decides afterwards whether the group
+// sees the tile.
 //
 // Exchange-tile columns are keys in the producer's register order: column
 // 16*hi + r holds key 8*(r/4) + 4*hi + (r%4), so a producer lane writes its
 // 16 values of one row as 32 contiguous bytes and the consumer's output
-// column c belongs to key kmap(c).  Rows have a stride of 48 elements, which
-// keeps the transposing reads free of bank conflicts.
+// column c belongs to key kmap(c).  Rows have a stride of 40 elements, which
+// keeps the producer's 16-lane write phases free of bank conflicts and lets
+// two sets of exchange tiles fit beside the ring.
 // ---------------------------------------------------------------------------
 namespace bwdkv {
 constexpr int NW = 8;          // waves per workgroup
 constexpr int KB = 128;        // keys per workgroup (4 key groups of 32)
 constexpr int TR = 32;         // query rows per tile
 constexpr int NST = 4;         // ring stages
-constexpr int XS = 48;         // row stride (elements) of an exchange tile
+constexpr int XS = 40;         // row stride (elements) of an exchange tile
 constexpr int MS = 64;         // stride (entries) of one meta array in a stage
 constexpr float kSplitP = 1.f / 256.f;
 __device__ __forceinline__ int kmap(int c) { return 8 * ((c & 15) >> 2) + 4 * (c >> 4) + (c & 3); }
@@ -418,10 +423,10 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
 
   __shared__ __attribute__((aligned(16))) uint16_t R[NST][2 * TS];   // Q | dO, rows x d, swizzled
   __shared__ __attribute__((aligned(16))) uint32_t Mr[NST][4 * MS];  // lse | delta | seq | pos
-  __shared__ __attribute__((aligned(16))) uint16_t X[4][4][XT];     // [group][P, dS, P lo, dS lo]
+  __shared__ __attribute__((aligned(16))) uint16_t X[2][4][4][XT];  // [tile parity][group][P, dS, P lo, dS lo]
   __shared__ __attribute__((aligned(16))) int kseq_s[KB];
   __shared__ __attribute__((aligned(16))) int kpos_s[KB];
-  __shared__ int Xf[4];   // per group: 0 nothing visible, 1 hi only, 2 hi + lo
+  __shared__ int Xf[2][4];   // per tile parity and group: 0 nothing visible, 1 hi only, 2 hi + lo
 
   const float scale_log2 = scale * kLog2e;
   const int nblk = (nk + KB - 1) / KB;
@@ -528,8 +533,8 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
       }
     }
     f32x16 sacc = zero16(), dpacc = zero16();
-    for (int i = 0; i <= ntiles; ++i) {
-      // half-step 1: tile i landed (the consumers waited for their loads of it)
+    for (int i = 0; i < ntiles; ++i) {
+      // tile i landed (the consumers waited for their loads of it)
       if (i > 0) wg_barrier<kWaitLgkm>();
       const int st = i % NST;
       int nrows = 0, fs = 0, fp = 0, ls = 0, lp = 0;
@@ -587,9 +592,7 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
                           !lex_less(kl_seq, INT_MAX, fs, fp);
       const bool full = wave_complete && nrows == TR && fs == ls && fs == kf_seq && kf_seq == kl_seq &&
                         fp >= kl_pos;
-      wg_barrier<kWaitLgkm>();
-      if (i == ntiles) break;
-      // half-step 2: softmax gradient of tile i -> exchange tiles of the group
+      // softmax gradient of tile i -> exchange tiles of the group (parity i)
       int flag = 0;
       if (active) {
         const float lse2 = lse_n * kLog2e;
@@ -625,7 +628,7 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
         // weight would otherwise carry bf16's 2^-9 relative rounding into the
         // key's gradient with a large coefficient.  Below the threshold the
         // dropped lo terms are at most kSplitP * 2^-9 each.
-        uint16_t* xrow = &X[kg][0][n * XS + 16 * hi];
+        uint16_t* xrow = &X[i & 1][kg][0][n * XS + 16 * hi];
         bf16x8 ph[2], dh[2];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -653,8 +656,10 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
           }
         }
       }
-      if (lane == 0) Xf[kg] = flag;
+      if (lane == 0) Xf[i & 1][kg] = flag;
     }
+    // the consumers read the last tile's exchange tiles after this barrier
+    if (ntiles > 0) wg_barrier<kWaitLgkm>();
     // every load of this workgroup has landed before its LDS is released
     wg_barrier<kWaitAll>();
   } else {
@@ -672,33 +677,32 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
     for (int i = 0; i <= ntiles; ++i) {
       // tile i landed: only this wave's newest batch (tile i+1) may be in flight
       if (i > 0) wg_barrier<wait_vm_lgkm<CROUNDS + 1>()>();
-      // half-step 1 (the producer's MFMAs): this iteration's loads, tile i+2
+      // this iteration's loads, tile i+2
       if (i < ntiles) issue((i + 2) % NST, min(i + 2, ntiles - 1));
       // and the exchange tiles of tile i-1 into registers
       int flag = 0;
       bf16x8 pop[2] = {zero8(), zero8()}, dop[2] = {zero8(), zero8()};
       bf16x8 plo[2] = {zero8(), zero8()}, dlo[2] = {zero8(), zero8()};
       if (i > 0) {
-        flag = __builtin_amdgcn_readfirstlane(Xf[kg]);
+        const int xp = (i - 1) & 1;   // exchange tiles of tile i-1
+        flag = __builtin_amdgcn_readfirstlane(Xf[xp][kg]);
         if (flag > 0) {
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
-            pop[s2] = tr_operand_at<XS>(&X[kg][0][0], 16 * s2, xo0, xo1);
-            dop[s2] = tr_operand_at<XS>(&X[kg][1][0], 16 * s2, xo0, xo1);
+            pop[s2] = tr_operand_at<XS>(&X[xp][kg][0][0], 16 * s2, xo0, xo1);
+            dop[s2] = tr_operand_at<XS>(&X[xp][kg][1][0], 16 * s2, xo0, xo1);
           }
           if (flag == 2) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-              plo[s2] = tr_operand_at<XS>(&X[kg][2][0], 16 * s2, xo0, xo1);
-              dlo[s2] = tr_operand_at<XS>(&X[kg][3][0], 16 * s2, xo0, xo1);
+              plo[s2] = tr_operand_at<XS>(&X[xp][kg][2][0], 16 * s2, xo0, xo1);
+              dlo[s2] = tr_operand_at<XS>(&X[xp][kg][3][0], 16 * s2, xo0, xo1);
             }
           }
         }
       }
-      // the exchange tiles are in registers before the producer rewrites them
-      wg_barrier<kWaitLgkm>();
       if (flag == 0) continue;
-      // half-step 2: dV^T += dO^T P, dK^T += Q^T dS over the 32 rows of tile
+      // dV^T += dO^T P, dK^T += Q^T dS over the 32 rows of tile
       // i-1; A operands (transposed Q / dO tiles) loaded kPre MFMAs ahead
       const uint16_t* prev = R[(i - 1) % NST];
       constexpr int NSTEP = 4 * MB;   // (tensor, k-step, d-block)
@@ -733,7 +737,7 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
           else acc_k[mb] = mfma32(a, dlo[s2], acc_k[mb]);
         }
       }
-      // the MFMAs stay in this half-step
+      // the MFMAs stay before the next barrier
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         keep(acc_v[mb]);
