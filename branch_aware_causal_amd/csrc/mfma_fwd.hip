@@ -17,10 +17,12 @@
 //     key visible to its last row], found by binary search on the (seq,
 //     pos)-sorted shard.  Within it the keys a row sees form one index
 //     interval, also found by binary search, so masks are index compares.
-//   * Ping-pong: waves w and w+4 share a SIMD and run one half-step apart
-//     (barrier between half-steps), so that while one issues the tile's 32
-//     MFMAs the other runs its softmax on the vector ALUs.  The MFMA stream
-//     runs at raised wave priority, so the partner's vector work yields to it.
+//   * Ping-pong: waves w and w+4 share a SIMD; in each tile period one runs
+//     its MFMA stream and then its softmax, the other its softmax and then
+//     its MFMA stream, so that while one issues the tile's MFMAs the other
+//     runs its softmax on the vector ALUs.  One barrier per tile period.  The
+//     MFMA stream runs at raised wave priority, so the partner's vector work
+//     yields to it.
 //   * Scores are computed transposed, S^T = K Q^T (keys x rows), so each lane
 //     holds 32 scores of ONE query row: the row max is in-lane plus one
 //     exchange with lane n+32, and the row sums stay per lane until the end.
@@ -167,18 +169,18 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
 
   // ---- ping-pong schedule ------------------------------------------------
   // Waves w and w+4 share a SIMD.  Team 0 (waves 0-3) and team 1 (waves 4-7)
-  // run the same sequence of half-steps, team 1 one half-step behind, with a
-  // workgroup barrier between half-steps, so that on every SIMD one wave
-  // feeds the matrix core while the other runs the softmax:
-  //   half-step 2t   : team 0 MFMA(t) = PV(t-1), S(t)   team 1 softmax(t-1)
-  //   half-step 2t+1 : team 0 softmax(t)                 team 1 MFMA(t)
-  // K(t) is read in half-steps 2t and 2t+1, V(t) in 2t+2 and 2t+3.  Team 0
-  // issues K(t+1) and V(t) at the start of half-step 2t and waits for them
-  // before the barrier that ends half-step 2t+1, so both are double buffered.
+  // run one tile period between workgroup barriers, in opposite orders, so
+  // that on every SIMD one wave feeds the matrix core while the other runs
+  // the softmax:
+  //   period t: team 0  MFMA(t) = PV(t-1), S(t), then softmax(t)
+  //             team 1  softmax(t-1), then MFMA(t)
+  // K(t) and V(t-1) are read in period t.  Team 0 issues K(t+1) and V(t)
+  // during its MFMA stream of period t and waits for them at the barrier that
+  // ends it, so both are double buffered.  (A barrier between the MFMA and
+  // softmax halves of a period cost 2.3% more time at 256K.)
   const int team = wave >> 2;
   if (team == 0 && ntiles > 0) issue_rows(k, &Ks[0][0], lo);
   wg_barrier<kWaitAll>();
-  if (team == 1) wg_barrier<kWaitNone>();
 
   f32x16 sacc[NKB];
   bf16x8 pb[2 * NKB];
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
     pb[2 * kb + 1] = zero8();
   }
 
-  // One MFMA half-step as a single stream: O^T += V^T P^T for tile t-1
+  // One MFMA stream of a period: O^T += V^T P^T for tile t-1
   // (2*NKB*MB MFMAs, transposed V operands), then S^T = K Q^T for tile t
   // (NKB*KS MFMAs, the NKB 32-key blocks interleaved).  LDS operands are read
   // kPre MFMAs ahead.  (Tiles of 128 keys rather than 64 halve the barriers
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
       else if (j + kPre < N)
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    // the stream stays in its half-step
+    // the stream stays before the softmax of the period
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) keep(oacc[mb]);
 #pragma unroll
@@ -262,8 +264,8 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // softmax half-step of the tile at j0: scores -> P (bf16) in pb; a tile
-  // this wave skips leaves zeros, so the next MFMA half-step may run its PV
+  // softmax of the tile at j0: scores -> P (bf16) in pb; a tile this wave
+  // skips leaves zeros, so the next MFMA stream may run its PV
   // regardless
   auto softmax = [&](int j0, bool do_s) {
     if (!do_s) {
@@ -315,25 +317,29 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
     keep(l_run);
   };
 
-  // t = 0: S(0) only
-  bool any_prev = false;
+  // One barrier per period t: team 0 runs MFMA(t) then softmax(t), team 1
+  // softmax(t-1) then MFMA(t), so on every SIMD one wave's MFMA stream meets
+  // the other's softmax without a barrier between them.  Team 0 loads K(t+1)
+  // and V(t) during period t and waits for them at the barrier that ends it;
+  // past the last tile K repeats the last tile into the buffer of K(t-1),
+  // which no later period reads.
+  bool any_prev = false;   // the previous tile was visible to the wave
+  // (the first and last periods are peeled: inside the loop the register
+  // allocator then keeps each team's live set to what its order needs)
   if (ntiles > 0) {
+    // period 0: S(0)
+    const bool do_s = tile_any(lo);
     if (team == 0) {
       if (ntiles > 1) issue_rows(k, &Ks[1][0], lo + BN);
       issue_rows(v, &Vs[0][0], lo);
     }
-    const bool do_s = tile_any(lo);
     if (do_s)
       mfma_stream(BoolC<false>(), BoolC<true>(), BoolC<false>(), &Vs[1][0], &Ks[0][0], nullptr, 0, nullptr,
                   0);
-    wg_barrier<kWaitNone>();
-    softmax(lo, do_s);
+    if (team == 0) softmax(lo, do_s);
     any_prev = do_s;
-    wg_barrier<kWaitAll>();     // team 0's loads of this tile pair have landed
+    wg_barrier<kWaitAll>();
   }
-  // 0 < t < ntiles: PV(t-1) and S(t) as one stream
-  // team 0 loads K(t+1) and V(t); past the last tile K repeats the last tile
-  // into the buffer of K(t-1), which no later half-step reads
   for (int t = 1; t < ntiles; ++t) {
     const int j0 = lo + t * BN;
     const int kj0 = min(j0 + BN, lo + (ntiles - 1) * BN);
@@ -349,20 +355,22 @@ __global__ __launch_bounds__(512, 1) void main_fwd_mfma_kernel(
         issue_rows(k, kdst, kj0);
         issue_rows(v, vdst, j0);
       }
-    } else if (any_prev || do_s) {
-      mfma_stream(BoolC<true>(), BoolC<true>(), BoolC<false>(), vt, kt, kdst, kj0, vdst, j0);
+      softmax(j0, do_s);
+    } else {
+      softmax(j0 - BN, any_prev);
+      if (any_prev || do_s)
+        mfma_stream(BoolC<true>(), BoolC<true>(), BoolC<false>(), vt, kt, kdst, kj0, vdst, j0);
     }
-    wg_barrier<kWaitNone>();
-    softmax(j0, do_s);
     any_prev = do_s;
     wg_barrier<kWaitAll>();
   }
-  // t = ntiles: PV(ntiles-1) only
-  if (any_prev)
-    mfma_stream(BoolC<true>(), BoolC<false>(), BoolC<false>(), &Vs[(ntiles - 1) & 1][0], &Ks[0][0], nullptr,
-                0, nullptr, 0);
-  wg_barrier<kWaitNone>();
-  if (team == 0) wg_barrier<kWaitNone>();
+  // period ntiles: PV(ntiles-1) (team 1 first finishes softmax(ntiles-1))
+  if (ntiles > 0) {
+    if (team == 1) softmax(lo + (ntiles - 1) * BN, any_prev);
+    if (any_prev)
+      mfma_stream(BoolC<true>(), BoolC<false>(), BoolC<false>(), &Vs[(ntiles - 1) & 1][0], &Ks[0][0],
+                  nullptr, 0, nullptr, 0);
+  }
 
   // ---- epilogue: normalise, merge, store ---------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
