@@ -555,7 +555,7 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
         // holds key 8*(r/4) + 4*hi + (r%4) of row n.  Computed for every
         // tile; used only if the group sees some of its rows.
         const uint16_t* cur = R[st];
-        constexpr int kPre = 8;
+        constexpr int kPre = 6;   // operands read ahead (6 and 8 measured alike, 12 slower)
         bf16x8 opnd[kPre];
         auto load = [&](int j) { return row_operand<D>(cur + (j & 1) * TS, lo_off, 0, j >> 1); };
 #pragma unroll
@@ -706,7 +706,7 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
       // i-1; A operands (transposed Q / dO tiles) loaded kPre MFMAs ahead
       const uint16_t* prev = R[(i - 1) % NST];
       constexpr int NSTEP = 4 * MB;   // (tensor, k-step, d-block)
-      constexpr int kPre = 4;
+      constexpr int kPre = 6;   // operands read ahead (4 measured 3.5% slower at 256K)
       auto load = [&](int j) {
         const int tsr = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
         return tr_operand<D>(prev + (tsr == 0 ? TS : 0), lo_off, 16 * s2, mb);
