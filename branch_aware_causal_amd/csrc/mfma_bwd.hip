@@ -40,20 +40,23 @@ constexpr int NW = 8;
 //     are one index interval of the (seq, pos)-sorted shard, found by binary
 //     search, so masks are index compares.
 //   * Ping-pong: waves w and w+4 share a SIMD; team 0 (waves 0-3) and team 1
-//     (waves 4-7) run the same half-steps one apart with a barrier between
-//     half-steps:
-//       half-step 2t   : team 0 MFMA(t)             team 1 GRAD(t-1)
-//       half-step 2t+1 : team 0 GRAD(t)             team 1 MFMA(t)
-//     MFMA(t) = dQ^T += K^T dS^T for tile t-1, then S^T = K Q^T and
-//     dP^T = V dO^T for tile t, as one stream of 48 MFMAs with LDS operands
-//     read ahead; GRAD(t) = dS = P (dP - Delta) on the vector ALUs.  K(t) is
-//     read in half-steps 2t .. 2t+3, V(t) in 2t and 2t+1.  Team 0 loads
-//     K(t+1) and V(t+1) at the start of half-step 2t and waits for them
-//     before the barrier that ends half-step 2t+1.
+//     (waves 4-7) run the same iteration -- MFMA(t), then GRAD(t) -- with
+//     one workgroup barrier per tile period, which team 0 passes after
+//     GRAD(t) and team 1 after MFMA(t).  So between two barriers
+//       team 0: MFMA(t) then GRAD(t)      team 1: GRAD(t-1) then MFMA(t)
+//     and on every SIMD one wave's MFMAs meet the other's vector work.
+//     (A barrier between the MFMA and GRAD halves cost 1.6% more time at
+//     256K; both teams run the same code, so the register allocator sees
+//     one live set.)  MFMA(t) = dQ^T += K^T dS^T for tile t-1, then
+//     S^T = K Q^T and dP^T = V dO^T for tile t, as one stream of 48 MFMAs
+//     with LDS operands read ahead; GRAD(t) = dS = P (dP - Delta) on the
+//     vector ALUs.  K(t) is read in periods t and t+1, V(t) in period t.
+//     Team 0 loads K(t+1) and V(t+1) at the start of its iteration t and
+//     waits for them at its barrier.
 //   * A wave reads the first K^T operands of its next MFMA stream at the end
-//     of its GRAD half-step (it has slack there), and runs its MFMA streams
-//     at raised issue priority so that the partner's vector work yields to
-//     them on the shared SIMD.
+//     of its GRAD step (it has slack there), and runs its MFMA streams at
+//     raised issue priority so that the partner's vector work yields to them
+//     on the shared SIMD.
 template <int D, int G>
 __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ q_seq,
@@ -168,18 +171,17 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
     issue_rows(v, &Vs[0][0], lo);
   }
   wg_barrier<kWaitAll>();     // also publishes the dO rows
-  if (team == 1) wg_barrier<kWaitNone>();
 
   f32x16 sacc[2] = {zero16(), zero16()}, dpacc[2] = {zero16(), zero16()};
   bf16x8 db[4] = {zero8(), zero8(), zero8(), zero8()};
 
-  // One MFMA half-step as a single stream: dQ^T += K^T dS^T for the previous
+  // One MFMA step as a single stream: dQ^T += K^T dS^T for the previous
   // tile (4*MB MFMAs, transposed K operands), then S^T = K Q^T and
   // dP^T = V dO^T for this tile (4*KS MFMAs, alternating).  LDS operands are
   // read kPre MFMAs ahead.
   constexpr int kPre = 2;
   // the first kPre operands of a stream that starts with dQ are read at the
-  // end of the wave's previous GRAD half-step (pre_dq), off the MFMA path
+  // end of the wave's previous GRAD step (pre_dq), off the MFMA path
   bf16x8 opa[kPre];
   auto pre_dq = [&](const uint16_t* kprev) {
 #pragma unroll
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
       else if (j + kPre < N)
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    // the stream stays in its half-step
+    // the stream stays before the GRAD step
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) keep(dqacc[mb]);
 #pragma unroll
@@ -252,8 +254,8 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
     }    __builtin_amdgcn_s_setprio(0);
   };
 
-  // GRAD half-step of the tile at j0: dS (bf16) into db; a tile this wave
-  // skips leaves zeros, so the next MFMA half-step may run its dQ regardless
+  // GRAD step of the tile at j0: dS (bf16) into db; a tile this wave skips
+  // leaves zeros, so the next MFMA step may run its dQ regardless
   auto grad = [&](int j0, bool do_s) {
     if (!do_s) {
 #pragma unroll
@@ -284,22 +286,25 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
     for (int i = 0; i < 4; ++i) keep(db[i]);
   };
 
-  // t = 0: S(0), dP(0) only
+  // One barrier per tile period, at a different place in each team's
+  // iteration: team 0 passes it after GRAD(t), team 1 after MFMA(t), so that
+  // between two barriers team 0 runs MFMA(t) then GRAD(t) while team 1 runs
+  // GRAD(t-1) then MFMA(t).  Team 0 loads K(t+1) and V(t+1) at the start of
+  // its iteration t and waits for them at its barrier.
   bool any_prev = false;
   if (ntiles > 0) {
-    if (team == 0) {
-      if (ntiles > 1) {
-        issue_rows(k, &Ks[1][0], lo + BN);
-        issue_rows(v, &Vs[1][0], lo + BN);
-      }
+    // t = 0: S(0), dP(0) only
+    if (team == 0 && ntiles > 1) {
+      issue_rows(k, &Ks[1][0], lo + BN);
+      issue_rows(v, &Vs[1][0], lo + BN);
     }
     const bool do_s = tile_any(lo);
     if (do_s) mfma_stream(BoolC<false>(), BoolC<true>(), &Ks[2][0], &Ks[0][0], &Vs[0][0]);
-    wg_barrier<kWaitNone>();
+    if (team == 1) wg_barrier<kWaitLgkm>();
     grad(lo, do_s);
     pre_dq(&Ks[0][0]);
     any_prev = do_s;
-    wg_barrier<kWaitAll>();     // team 0's loads of this tile pair have landed
+    if (team == 0) wg_barrier<kWaitAll>();     // team 0's loads of tile 1 have landed
   }
   // 0 < t < ntiles: dQ(t-1), S(t), dP(t) as one stream; c = t % 3
   int c = 1;
@@ -313,18 +318,16 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
     const bool do_s = tile_any(j0);
     if (any_prev || do_s)
       mfma_stream(BoolC<true>(), BoolC<true>(), &Ks[cp][0], &Ks[c][0], &Vs[t & 1][0]);
-    wg_barrier<kWaitNone>();
+    if (team == 1) wg_barrier<kWaitLgkm>();
     grad(j0, do_s);
     pre_dq(&Ks[c][0]);
     any_prev = do_s;
-    wg_barrier<kWaitAll>();
+    if (team == 0) wg_barrier<kWaitAll>();
     c = cn;
   }
   // t = ntiles: dQ(ntiles-1) only
   if (any_prev)
     mfma_stream(BoolC<true>(), BoolC<false>(), &Ks[(ntiles - 1) % 3][0], &Ks[0][0], &Vs[0][0]);
-  wg_barrier<kWaitNone>();
-  if (team == 0) wg_barrier<kWaitNone>();
 
   if (!row_valid) return;
   const size_t obase = (static_cast<size_t>(my_tok) * hq + my_head) * D;
