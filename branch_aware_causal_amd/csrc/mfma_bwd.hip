@@ -364,16 +364,19 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_kernel(
 // block of a sequence sees the same trailing rows, so the workgroups an XCD
 // runs together read the same tiles at nearly the same time, through L2).
 //
-// Eight waves in two teams; waves w and w+4 share a SIMD and serve key
-// group w:
-//   * producer (waves 0-3): K and V of the group's 32 keys in registers as
+// Eight waves in two teams; waves w and w+4 share a SIMD:
+//   * producer w (waves 0-3) serves key group w: K and V of the group's 32 keys in registers as
 //     MFMA A operands; per tile, S^T = K Q^T and dP^T = V dO^T (one query row
 //     per lane), then P = exp2(s*c - lse2) and dS = P (dP - Delta); P and dS
 //     go to LDS as bf16 [row][key] tiles (hi + lo pairs where some P of the
 //     tile reaches kSplitP, see below), with a flag per group;
-//   * consumer (waves 4-7): dV^T += dO^T P and dK^T += Q^T dS for the group
-//     over the tile's rows, both operands by transposing LDS reads, the
-//     accumulators in registers for the whole block.
+//   * consumer (waves 4-7): dV^T += dO^T P and dK^T += Q^T dS over the
+//     tile's rows, both operands by transposing LDS reads, the accumulators
+//     in registers for the whole block.  Consumer c covers key groups
+//     2*(c/2) and 2*(c/2)+1 for half of d (d-blocks 2*(c%2) ..): each
+//     transposed Q / dO operand then feeds two MFMAs, 32 transposing reads
+//     per tile instead of 40 with one group over all of d (0.6-1.5% less
+//     dK/dV time at 256K).
 // One barrier per tile.  In iteration i the producer runs the S / dP MFMAs
 // of tile i and then its softmax gradient (vector ALUs), writing the P / dS
 // tiles of tile i into exchange buffer i % 2; the consumer issues the loads
@@ -691,12 +694,27 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
     wg_barrier<kWaitAll>();
   } else {
     // ======================= consumer: dV, dK ===============================
-    f32x16 acc_v[MB], acc_k[MB];
+    // Consumer c serves key groups cg0 and cg0+1 over the d-blocks mb0 ..
+    // mb0+MH-1, so that each transposed Q / dO operand it reads feeds two
+    // MFMAs (one per key group).
+    constexpr int MH = MB / 2;              // d-blocks per consumer
+    const int cg0 = 2 * (kg >> 1);          // first key group
+    const int mb0 = MH * (kg & 1);          // first d-block
+    // transposed-read offsets of this consumer's d-blocks (selected, not
+    // indexed, so that they stay in registers)
+    int tro[MH][2];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      acc_v[mb] = zero16();
-      acc_k[mb] = zero16();
-    }
+    for (int mh = 0; mh < MH; ++mh)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) tro[mh][e] = (kg & 1) ? lo_off.tr[MH + mh][e] : lo_off.tr[mh][e];
+    f32x16 acc_v[2][MH], acc_k[2][MH];
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+      for (int mb = 0; mb < MH; ++mb) {
+        acc_v[gg][mb] = zero16();
+        acc_k[gg][mb] = zero16();
+      }
     // transposing reads of an exchange tile (one 32-column block)
     const int xg = lane >> 4, xi = lane & 15;
     const int xr0 = 4 * (xg >> 1) + (xi >> 2), xc0 = 16 * (xg & 1) + 4 * (xi & 3);
@@ -706,94 +724,120 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dkdv_kernel(
       if (i > 0) wg_barrier<wait_vm_lgkm<CROUNDS + 1>()>();
       // this iteration's loads, tile i+2
       if (i < ntiles) issue((i + 2) % NST, min(i + 2, ntiles - 1));
-      // and the exchange tiles of tile i-1 into registers
-      int flag = 0;
-      bf16x8 pop[2] = {zero8(), zero8()}, dop[2] = {zero8(), zero8()};
-      bf16x8 plo[2] = {zero8(), zero8()}, dlo[2] = {zero8(), zero8()};
+      // and the exchange tiles of tile i-1 into registers; a group that
+      // skips the tile contributes zeros
+      int fl[2] = {0, 0};
+      bf16x8 pop[2][2], dop[2][2];
       if (i > 0) {
         const int xp = (i - 1) & 1;   // exchange tiles of tile i-1
-        flag = __builtin_amdgcn_readfirstlane(Xf[xp][kg]);
-        if (flag > 0) {
+        fl[0] = __builtin_amdgcn_readfirstlane(Xf[xp][cg0]);
+        fl[1] = __builtin_amdgcn_readfirstlane(Xf[xp][cg0 + 1]);
+        if (fl[0] + fl[1] > 0) {
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            pop[s2] = tr_operand_at<XS>(&X[xp][kg][0][0], 16 * s2, xo0, xo1);
-            dop[s2] = tr_operand_at<XS>(&X[xp][kg][1][0], 16 * s2, xo0, xo1);
-          }
-          if (flag == 2) {
+          for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-              plo[s2] = tr_operand_at<XS>(&X[xp][kg][2][0], 16 * s2, xo0, xo1);
-              dlo[s2] = tr_operand_at<XS>(&X[xp][kg][3][0], 16 * s2, xo0, xo1);
+              pop[gg][s2] = tr_operand_at<XS>(&X[xp][cg0 + gg][0][0], 16 * s2, xo0, xo1);
+              dop[gg][s2] = tr_operand_at<XS>(&X[xp][cg0 + gg][1][0], 16 * s2, xo0, xo1);
             }
-          }
+#pragma unroll
+          for (int gg = 0; gg < 2; ++gg)
+            if (fl[gg] == 0) {
+#pragma unroll
+              for (int s2 = 0; s2 < 2; ++s2) {
+                pop[gg][s2] = zero8();
+                dop[gg][s2] = zero8();
+              }
+            }
         }
       }
-      if (flag == 0) continue;
-      // dV^T += dO^T P, dK^T += Q^T dS over the 32 rows of tile
-      // i-1; A operands (transposed Q / dO tiles) loaded kPre MFMAs ahead
+      if (fl[0] + fl[1] == 0) continue;
+      // dV^T += dO^T P, dK^T += Q^T dS over the 32 rows of tile i-1 for
+      // both groups; A operands (transposed Q / dO, indexed (tensor,
+      // k-step, d-block)) loaded kPre operands ahead
+      const int xp = (i - 1) & 1;
       const uint16_t* prev = R[(i - 1) % NST];
-      constexpr int NSTEP = 4 * MB;   // (tensor, k-step, d-block)
-      constexpr int kPre = 6;   // operands read ahead (4 measured 3.5% slower at 256K)
+      constexpr int NA = 4 * MH;   // A operands per tile
+      constexpr int kPre = NA < 4 ? NA : 4;
       auto load = [&](int j) {
-        const int tsr = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
-        return tr_operand<D>(prev + (tsr == 0 ? TS : 0), lo_off, 16 * s2, mb);
+        const int tsr = j / (2 * MH), s2 = (j / MH) % 2, mh = j % MH;
+        return tr_operand_at<D>(prev + (tsr == 0 ? TS : 0), 16 * s2, tro[mh][0], tro[mh][1]);
       };
       bf16x8 opnd[kPre];
 #pragma unroll
       for (int j = 0; j < kPre; ++j) opnd[j] = load(j);
 #pragma unroll
-      for (int j = 0; j < NSTEP; ++j) {
-        const int tsr = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
-        if (tsr == 0) acc_v[mb] = mfma32(opnd[j % kPre], pop[s2], acc_v[mb]);
-        else acc_k[mb] = mfma32(opnd[j % kPre], dop[s2], acc_k[mb]);
-        if (j + kPre < NSTEP) opnd[j % kPre] = load(j + kPre);
+      for (int j = 0; j < NA; ++j) {
+        const int tsr = j / (2 * MH), s2 = (j / MH) % 2, mh = j % MH;
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          if (tsr == 0) acc_v[gg][mh] = mfma32(opnd[j % kPre], pop[gg][s2], acc_v[gg][mh]);
+          else acc_k[gg][mh] = mfma32(opnd[j % kPre], dop[gg][s2], acc_k[gg][mh]);
+        }
+        if (j + kPre < NA) opnd[j % kPre] = load(j + kPre);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPre, 0);
 #pragma unroll
-      for (int j = 0; j < NSTEP - kPre; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      for (int j = 0; j < NA - kPre; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
-      if (flag == 2) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kPre, 0);
+      // lo pass of the groups whose P reaches kSplitP somewhere in the tile
 #pragma unroll
-        for (int j = 0; j < NSTEP; ++j) {
-          const int tsr = j / (2 * MB), s2 = (j / MB) % 2, mb = j % MB;
-          const bf16x8 a = tr_operand<D>(prev + (tsr == 0 ? TS : 0), lo_off, 16 * s2, mb);
-          if (tsr == 0) acc_v[mb] = mfma32(a, plo[s2], acc_v[mb]);
-          else acc_k[mb] = mfma32(a, dlo[s2], acc_k[mb]);
+      for (int gg = 0; gg < 2; ++gg) {
+        if (fl[gg] == 2) {
+          bf16x8 plo[2], dlo[2];
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            plo[s2] = tr_operand_at<XS>(&X[xp][cg0 + gg][2][0], 16 * s2, xo0, xo1);
+            dlo[s2] = tr_operand_at<XS>(&X[xp][cg0 + gg][3][0], 16 * s2, xo0, xo1);
+          }
+#pragma unroll
+          for (int j = 0; j < NA; ++j) {
+            const int tsr = j / (2 * MH), s2 = (j / MH) % 2, mh = j % MH;
+            const bf16x8 a = load(j);
+            if (tsr == 0) acc_v[gg][mh] = mfma32(a, plo[s2], acc_v[gg][mh]);
+            else acc_k[gg][mh] = mfma32(a, dlo[s2], acc_k[gg][mh]);
+          }
         }
       }
       // the MFMAs stay before the next barrier
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        keep(acc_v[mb]);
-        keep(acc_k[mb]);
-      }
+      for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+        for (int mh = 0; mh < MH; ++mh) {
+          keep(acc_v[gg][mh]);
+          keep(acc_k[gg][mh]);
+        }
     }
     wg_barrier<kWaitAll>();
-    // ---- store: output column n holds key kmap(n) ----------------------
-    const int my_key = wk0 + kmap(n);
-    if (my_key < nk) {
-      const size_t obase = (static_cast<size_t>(my_key) * hkv + g) * D;
+    // ---- store: output column n holds key kmap(n) of the group -----------
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+    for (int gg = 0; gg < 2; ++gg) {
+      const int my_key = key0 + 32 * (cg0 + gg) + kmap(n);
+      if (my_key < nk) {
+        const size_t obase = (static_cast<size_t>(my_key) * hkv + g) * D;
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          float4* pv = reinterpret_cast<float4*>(dv + obase + mb * 32 + 8 * gq + 4 * hi);
-          float4* pk = reinterpret_cast<float4*>(dk + obase + mb * 32 + 8 * gq + 4 * hi);
-          float4 a = *pv, b = *pk;
-          a.x += acc_v[mb][4 * gq + 0];
-          a.y += acc_v[mb][4 * gq + 1];
-          a.z += acc_v[mb][4 * gq + 2];
-          a.w += acc_v[mb][4 * gq + 3];
-          b.x += scale * acc_k[mb][4 * gq + 0];
-          b.y += scale * acc_k[mb][4 * gq + 1];
-          b.z += scale * acc_k[mb][4 * gq + 2];
-          b.w += scale * acc_k[mb][4 * gq + 3];
-          *pv = a;
-          *pk = b;
-        }
+        for (int mh = 0; mh < MH; ++mh)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int col = (mb0 + mh) * 32 + 8 * gq + 4 * hi;
+            float4* pv = reinterpret_cast<float4*>(dv + obase + col);
+            float4* pk = reinterpret_cast<float4*>(dk + obase + col);
+            float4 a = *pv, b = *pk;
+            a.x += acc_v[gg][mh][4 * gq + 0];
+            a.y += acc_v[gg][mh][4 * gq + 1];
+            a.z += acc_v[gg][mh][4 * gq + 2];
+            a.w += acc_v[gg][mh][4 * gq + 3];
+            b.x += scale * acc_k[gg][mh][4 * gq + 0];
+            b.y += scale * acc_k[gg][mh][4 * gq + 1];
+            b.z += scale * acc_k[gg][mh][4 * gq + 2];
+            b.w += scale * acc_k[gg][mh][4 * gq + 3];
+            *pv = a;
+            *pk = b;
+          }
+      }
     }
   }
 }
